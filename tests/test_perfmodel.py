@@ -1,0 +1,59 @@
+"""Measurement helpers against the worked numbers the pages print (tests/golden)."""
+
+import json
+import os
+
+import pytest
+
+from tiled_attention_17_amd import perfmodel as pm
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_worked_numbers.json")))
+
+
+def test_roofline_worked_example():
+    g = GOLD["roofline_example"]
+    ai = pm.intensity(g["flops"], g["bytes"])
+    assert ai == g["intensity"]
+    assert pm.roofline_bound(1e15, g["bandwidth_bytes_per_s"], ai) == g["bound_flops_per_s"]
+
+
+def test_wave_quantization_example():
+    g = GOLD["wave_quantization"]
+    ta = pm.tiles(g["size_a"], g["size_a"], g["tile_m"], g["tile_n"])
+    tb = pm.tiles(g["size_b"], g["size_b"], g["tile_m"], g["tile_n"])
+    assert (ta, tb) == (g["tiles_a"], g["tiles_b"])
+    assert pm.waves(ta, g["units"]) == 1
+    assert pm.waves(tb, g["units"]) == g["waves_b"]
+    assert pm.tail_tiles(tb, g["units"]) == g["tail_b"]
+
+
+def test_low_precision_traffic():
+    g = GOLD["low_precision_traffic"]
+    # ReLU: one FLOP per element, one read and one write of the element.
+    assert 1 / pm.intensity(1, 4 + 4) == g["fp32_bytes_per_flop"]
+    assert 1 / pm.intensity(1, 2 + 2) == g["bf16_bytes_per_flop"]
+
+
+def test_tiling_reads():
+    g = GOLD["tiling_reads"]
+    assert g["n"] // g["t"] == g["tiled_reads"]
+    assert g["untiled_reads"] == g["n"]
+
+
+def test_matmul_counts():
+    assert pm.matmul_flops(2, 3, 4) == 48
+    assert pm.matmul_min_bytes(2, 3, 4) == 2 * (6 + 12 + 8)
+
+
+@pytest.mark.parametrize("B,H,N,d,e,flops,nbytes", [
+    (1, 1, 256, 64, 4, 16_777_216, 263_168),
+    (4, 8, 1024, 64, 2, 8_589_934_592, 16_908_288),
+    (2, 16, 4096, 128, 2, 274_877_906_944, 134_742_016),
+    (1, 16, 16384, 128, 2, 2_199_023_255_552, 269_484_032),
+])
+def test_attention_counts(B, H, N, d, e, flops, nbytes):
+    assert pm.attn_fwd_flops(B, H, N, d) == flops
+    assert pm.attn_fwd_bytes(B, H, N, d, e) == nbytes
+    # each forward FLOP count is two matmuls per head
+    assert pm.attn_fwd_flops(B, H, N, d) == B * H * (pm.matmul_flops(N, d, N) + pm.matmul_flops(N, N, d))
+    assert pm.attn_bwd_flops(B, H, N, d) == B * H * 5 * pm.matmul_flops(N, d, N)

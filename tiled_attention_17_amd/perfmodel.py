@@ -1,0 +1,77 @@
+"""Work, traffic and roofline arithmetic for the attention kernels.
+
+Counting rules, from the Lecture 17 page (§5.3: a matmul of M x K by K x N
+costs about 2MKN floating-point operations and, with 16-bit elements read
+once and written once, at least 2(MK + KN + MN) bytes; §6.1: arithmetic
+intensity is FLOPs per byte moved at a stated memory level; §6.2: the
+roofline bound is min(peak, bandwidth x intensity)) and from the CS336
+Lecture 5 notes §6.2 (wave quantization: tiles beyond a whole number of
+waves over the compute units leave the chip mostly idle).
+"""
+
+from __future__ import annotations
+
+import math
+
+# MI355X (gfx950) published figures.
+MI355X_CUS = 256
+MI355X_XCDS = 8
+MI355X_CLOCK_HZ = 2.4e9
+MI355X_HBM_BYTES_PER_S = 8.0e12
+MI355X_PEAK_FLOPS = {
+    "bf16": 2.5e15,   # dense MFMA
+    "fp16": 2.5e15,
+    "fp32": 157.3e12,  # fp32 matrix
+}
+
+
+def matmul_flops(m, k, n):
+    return 2 * m * k * n
+
+
+def matmul_min_bytes(m, k, n, elem_bytes=2):
+    return elem_bytes * (m * k + k * n + m * n)
+
+
+def intensity(flops, nbytes):
+    return flops / nbytes
+
+
+def roofline_bound(peak_flops, bandwidth, ai):
+    return min(peak_flops, bandwidth * ai)
+
+
+def tiles(m, n, tile_m, tile_n):
+    return math.ceil(m / tile_m) * math.ceil(n / tile_n)
+
+
+def waves(n_tiles, units):
+    return math.ceil(n_tiles / units)
+
+
+def tail_tiles(n_tiles, units):
+    """Tiles in the last, partial wave (0 when the tiles fill whole waves)."""
+    r = n_tiles % units
+    return r
+
+
+def attn_fwd_flops(B, H, N, d, Nk=None):
+    """Two matmuls per head: S = Q K^T and O = P V, 2*N*Nk*d each."""
+    Nk = N if Nk is None else Nk
+    return 4 * B * H * N * Nk * d
+
+
+def attn_bwd_flops(B, H, N, d, Nk=None):
+    """Five matmuls per head: recomputed Q K^T, P^T dO, dO V^T, dS K, dS^T Q."""
+    Nk = N if Nk is None else Nk
+    return 10 * B * H * N * Nk * d
+
+
+def attn_fwd_bytes(B, H, N, d, elem_bytes):
+    """Read Q, K, V once, write O once, write the fp32 LSE once."""
+    return B * H * (4 * N * d * elem_bytes + 4 * N)
+
+
+def attn_bwd_bytes(B, H, N, d, elem_bytes):
+    """Read Q, K, V, O, dO and write dQ, dK, dV once; LSE read, row term D written and read (fp32)."""
+    return B * H * (8 * N * d * elem_bytes + 3 * N * 4)
