@@ -1,0 +1,121 @@
+/*
+ * tiled_attn.h -- C ABI of the fused softmax-attention library for MI355X (gfx950).
+ *
+ * What is computed. For every (batch b, head h) slice, with S = scale * Q K^T:
+ *   O   = softmax(S) V                       (row softmax over the keys)
+ *   LSE = ln sum_j exp(S_ij)                 (natural log, one value per query row)
+ * as defined by the Lecture 17 page "Tensor Core, HBM, SRAM and FlashAttention"
+ * §8.1 (scaled dot-product attention) and computed the way its §8.2-§8.3
+ * describe: Q, K and V are tiled, each score tile is formed on chip, a running
+ * row maximum and sum are rescaled online, and the full N x N score and
+ * probability matrices never reach device memory. The backward entry point
+ * returns the exact gradients of sum(O * dO) and, as the CS336 Lecture 5
+ * notes §7.2 ("Recomputation") describe, recomputes the score tiles from the
+ * saved LSE instead of storing them.
+ *
+ * Layout. Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] arrays
+ * (d innermost, no strides); LSE is a dense [B, H, N] float array. Every
+ * pointer is a device pointer. Q, K and V share N (self-attention shape).
+ *
+ * Supported: d in {64, 128}; N >= 1 (any N; a ragged last tile is masked);
+ * element type bfloat16 (ATTN_BF16; inputs and outputs bf16, all softmax
+ * arithmetic and accumulation in fp32) or float (ATTN_FP32; fp32 everywhere,
+ * forward only); scale finite and >= 0. A call with B*H*N == 0 does nothing
+ * and returns ATTN_OK.
+ *
+ * Ownership. The caller owns every buffer, including the backward workspace.
+ * The library allocates and frees nothing and keeps no per-call state.
+ *
+ * Execution. Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without waiting: results are valid once the
+ * stream has been synchronised. Calls on different streams that write the
+ * same buffers race.
+ *
+ * Errors. Every argument is validated on the host before anything is
+ * enqueued: on a failed check the call returns ATTN_ERR_INVALID_ARGUMENT or
+ * ATTN_ERR_UNSUPPORTED, launches nothing, leaves all outputs untouched, and
+ * attn_last_error() (per host thread) describes the problem. A failed kernel
+ * launch returns ATTN_ERR_HIP with the HIP error text. No C++ exception
+ * crosses this interface.
+ */
+#ifndef TILED_ATTN_H_
+#define TILED_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, negative size, aliasing, bad scale ... */
+  ATTN_ERR_UNSUPPORTED = 2,      /* a valid request this library does not implement (e.g. d = 96) */
+  ATTN_ERR_HIP = 3               /* the HIP runtime reported an error while enqueuing */
+} attn_status;
+
+typedef enum {
+  ATTN_BF16 = 0, /* bfloat16 storage, fp32 arithmetic */
+  ATTN_FP32 = 1  /* float storage and arithmetic */
+} attn_dtype;
+
+/* Library interface version (increments on any ABI change). */
+int attn_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* attn_status_string(attn_status status);
+
+/* Detail of the last failed call on this host thread ("" if none). The
+ * returned string stays valid until the next library call on this thread. */
+const char* attn_last_error(void);
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T) V and LSE, per (b, h).
+ *   q, k, v  [B,H,N,d] inputs of type `dtype`, 16-byte aligned.
+ *   o        [B,H,N,d] output of type `dtype`, 16-byte aligned; must not
+ *            overlap any input.
+ *   lse      [B,H,N] float output, 16-byte aligned; LSE_i = ln sum_j
+ *            exp(scale * q_i . k_j) (the log of the softmax denominator, as
+ *            the online statistics m + ln l of the Lecture 17 page §8.3).
+ * Source: Lecture 17 page §8.1 (definition), §8.2 (tiled, IO-aware flow),
+ * §8.3 (online softmax update m' = max(m, max s), alpha = e^(m - m'),
+ * l' = alpha l + sum p, o' = alpha o + p V, O = o / l).
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     attn_dtype dtype, void* stream);
+
+/* Bytes of device workspace attn_bwd needs for these sizes (the per-row
+ * term D_i = sum_k dO_ik O_ik, one float per query row). */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype dtype);
+
+/*
+ * Backward pass: the gradients of sum(O * dO) with respect to Q, K, V.
+ *   q, k, v, o, dout   [B,H,N,d] inputs (o and lse as returned by attn_fwd
+ *                      for the same q, k, v, scale), 16-byte aligned.
+ *   lse                [B,H,N] float input.
+ *   dq, dk, dv         [B,H,N,d] outputs of type `dtype` (fp32 accumulation,
+ *                      rounded once); must not overlap any input or each other.
+ *   workspace          device scratch of at least attn_bwd_workspace_bytes()
+ *                      bytes, 16-byte aligned, owned by the caller; its
+ *                      contents on entry are ignored.
+ * The score and probability tiles are recomputed from q, k and lse; no
+ * N x N matrix is stored (CS336 Lecture 5 notes §7.2 "Recomputation"; the
+ * CS336 2026 Lecture 05 note, "FlashAttention 解析" ②). Gradient formulas are
+ * the exact derivative of the forward definition:
+ *   dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i, dS = P * (dP - D),
+ *   dQ = scale dS K, dK = scale dS^T Q.
+ * bf16 only (ATTN_FP32 returns ATTN_ERR_UNSUPPORTED).
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     attn_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILED_ATTN_H_ */

@@ -1,0 +1,161 @@
+"""Fused softmax attention for MI355X (gfx950): Python binding of libtiledattn.so.
+
+The functions here only marshal arguments: they check tensor metadata,
+allocate outputs with torch (device memory), and call the C-ABI entry points
+of the same names declared in include/tiled_attn.h on the current HIP
+stream. Every step of the computation runs in the library's HIP kernels;
+there is no fallback. If the library has not been built, calling any of them
+raises immediately.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "library", "AttnError",
+           "ATTN_BF16", "ATTN_FP32", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtiledattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_BF16, ATTN_FP32 = 0, 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def library():
+    """The loaded libtiledattn.so (ctypes), loading it on first use."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run __graft_entry__.build() or python tiled_attention_17_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_i64, c_vp, c_f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.attn_version.restype = ctypes.c_int
+    lib.attn_version.argtypes = []
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_f,
+                             ctypes.c_int, c_vp]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                             ctypes.c_size_t, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int, c_vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = library()
+        msg = lib.attn_last_error().decode() or lib.attn_status_string(status).decode()
+        raise AttnError(status, msg)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _shape4(name, t, shape=None, dtype=None, device=None):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d], got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def attn_fwd(q, k, v, scale=None, *, out=None, lse=None, stream=None):
+    """O, LSE = attention forward of [B, H, N, d] tensors q, k, v (see attn_fwd in tiled_attn.h).
+
+    scale defaults to 1/sqrt(d). Returns (O like q, LSE float32 [B, H, N]).
+    """
+    import torch
+    lib = library()
+    _shape4("q", q)
+    shape, dt, dev = tuple(q.shape), q.dtype, q.device
+    _shape4("k", k, shape, dt, dev)
+    _shape4("v", v, shape, dt, dev)
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    B, H, N, d = shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _shape4("out", out, shape, dt, dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    with torch.cuda.device(dev):
+        st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, float(scale), _dtype_code(q), _stream(dev, stream))
+    _check(st)
+    return out, lse
+
+
+def attn_bwd_workspace_bytes(B, H, N, d, dtype_code=ATTN_BF16):
+    return int(library().attn_bwd_workspace_bytes(B, H, N, d, dtype_code))
+
+
+def attn_bwd(q, k, v, o, do, lse, scale=None, *, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """dQ, dK, dV of sum(O * dO) (see attn_bwd in tiled_attn.h). bf16 tensors [B, H, N, d]."""
+    import torch
+    lib = library()
+    _shape4("q", q)
+    shape, dt, dev = tuple(q.shape), q.dtype, q.device
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _shape4(name, t, shape, dt, dev)
+    B, H, N, d = shape
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _shape4(name, t, shape, dt, dev)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          B, H, N, d, float(scale), code, _stream(dev, stream))
+    _check(st)
+    return dq, dk, dv

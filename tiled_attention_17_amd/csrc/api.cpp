@@ -1,0 +1,214 @@
+// C-ABI layer: argument validation, diagnostics and dispatch to the kernels.
+// Every check runs on the host before any HIP call, so a rejected call
+// enqueues nothing and touches no output.
+#include "tiled_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status fail(attn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status fail(attn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+attn_status ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo;
+  uintptr_t hi;  // exclusive
+};
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Sizes shared by both entry points. Fills `elems` (elements per tensor)
+// and `rows` (B*H*N) when the shape is valid.
+attn_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype dtype,
+                        int64_t* elems, int64_t* rows) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  if (B < 0 || H < 0 || N < 0 || d < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld N=%lld d=%lld)",
+                (long long)B, (long long)H, (long long)N, (long long)d);
+  if (d != 64 && d != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%lld is not supported (64 or 128)",
+                (long long)d);
+  if (N > (int64_t(1) << 30))
+    return fail(ATTN_ERR_UNSUPPORTED, "sequence length N=%lld exceeds 2^30", (long long)N);
+  if (B > (int64_t(1) << 30) || H > (int64_t(1) << 30) || (B && H && B * H > (int64_t(1) << 31)))
+    return fail(ATTN_ERR_UNSUPPORTED, "B*H too large (B=%lld H=%lld)", (long long)B, (long long)H);
+  const int64_t bh = B * H;
+  if (bh && N && bh > (INT64_MAX / 8) / N / d)
+    return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+  *rows = bh * N;
+  *elems = *rows * d;
+  return ATTN_OK;
+}
+
+attn_status check_ptr(const void* p, const char* name, uintptr_t align) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if ((uintptr_t)p % align)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "%s=%p is not %zu-byte aligned", name, p, (size_t)align);
+  return ATTN_OK;
+}
+
+attn_status check_scale(float scale) {
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0 (got %g)", (double)scale);
+  return ATTN_OK;
+}
+
+// Compute units of the current device, cached per device id.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+attn_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) {
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return ATTN_OK;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return ATTN_OK;
+}
+
+int env_waves() {
+  const char* s = std::getenv("TILED_ATTN_FWD_WAVES");
+  if (!s) return 0;
+  const int w = std::atoi(s);
+  return (w == 2 || w == 4 || w == 8) ? w : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return 1; }
+
+const char* attn_status_string(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_STATUS_UNKNOWN";
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t H, int64_t N, int64_t d, float scale, attn_dtype dtype,
+                     void* stream) {
+  int64_t elems = 0, rows = 0;
+  attn_status s = check_shape(B, H, N, d, dtype, &elems, &rows);
+  if (s != ATTN_OK) return s;
+  if ((s = check_scale(scale)) != ATTN_OK) return s;
+  if (rows == 0) return ok();
+  if ((s = check_ptr(q, "q", 16)) != ATTN_OK || (s = check_ptr(k, "k", 16)) != ATTN_OK ||
+      (s = check_ptr(v, "v", 16)) != ATTN_OK || (s = check_ptr(o, "o", 16)) != ATTN_OK ||
+      (s = check_ptr(lse, "lse", 16)) != ATTN_OK)
+    return s;
+  const uintptr_t tb = (uintptr_t)elems * (dtype == ATTN_FP32 ? 4 : 2);
+  const Range in[3] = {{"q", (uintptr_t)q, (uintptr_t)q + tb},
+                       {"k", (uintptr_t)k, (uintptr_t)k + tb},
+                       {"v", (uintptr_t)v, (uintptr_t)v + tb}};
+  const Range out[2] = {{"o", (uintptr_t)o, (uintptr_t)o + tb},
+                        {"lse", (uintptr_t)lse, (uintptr_t)lse + (uintptr_t)rows * 4}};
+  for (const Range& a : out)
+    for (const Range& b : in)
+      if (overlaps(a, b)) return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", a.name, b.name);
+  if (overlaps(out[0], out[1])) return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs o and lse overlap");
+
+  int cus = 0;
+  if ((s = device_cus(&cus)) != ATTN_OK) return s;
+  tattn::FwdArgs a{q, k, v, o, lse, B * H, N, d, scale, dtype == ATTN_FP32, stream, cus, env_waves()};
+  const hipError_t e = tattn::launch_attn_fwd(a);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype dtype) {
+  int64_t elems = 0, rows = 0;
+  if (check_shape(B, H, N, d, dtype, &elems, &rows) != ATTN_OK) return 0;
+  return (size_t)rows * sizeof(float);
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                     float scale, attn_dtype dtype, void* stream) {
+  int64_t elems = 0, rows = 0;
+  attn_status s = check_shape(B, H, N, d, dtype, &elems, &rows);
+  if (s != ATTN_OK) return s;
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
+  if ((s = check_scale(scale)) != ATTN_OK) return s;
+  if (rows == 0) return ok();
+  const struct { const void* p; const char* n; } ins[] = {
+      {q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}};
+  const struct { const void* p; const char* n; } outs[] = {
+      {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {workspace, "workspace"}};
+  for (auto& x : ins)
+    if ((s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
+  for (auto& x : outs)
+    if ((s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
+  const size_t need = (size_t)rows * sizeof(float);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  const uintptr_t tb = (uintptr_t)elems * 2, lb = (uintptr_t)rows * 4;
+  Range rin[6], rout[4];
+  for (int i = 0; i < 6; ++i)
+    rin[i] = {ins[i].n, (uintptr_t)ins[i].p, (uintptr_t)ins[i].p + (i == 5 ? lb : tb)};
+  for (int i = 0; i < 4; ++i)
+    rout[i] = {outs[i].n, (uintptr_t)outs[i].p, (uintptr_t)outs[i].p + (i == 3 ? need : tb)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(rout[i], rin[j]))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", rout[i].name, rin[j].name);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(rout[i], rout[j]))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs %s and %s overlap", rout[i].name, rout[j].name);
+  }
+
+  int cus = 0;
+  if ((s = device_cus(&cus)) != ATTN_OK) return s;
+  tattn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B * H, N, d, scale, stream, cus};
+  const hipError_t e = tattn::launch_attn_bwd(a);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
