@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "launch.h"
@@ -103,6 +104,15 @@ attn_status device_cus(int* cus) {
   return ATTN_OK;
 }
 
+int env_int(const char* name, std::initializer_list<int> allowed) {
+  const char* s = std::getenv(name);
+  if (!s) return 0;
+  const int w = std::atoi(s);
+  for (int a : allowed)
+    if (w == a) return w;
+  return 0;
+}
+
 int env_waves() {
   const char* s = std::getenv("TILED_ATTN_FWD_WAVES");
   if (!s) return 0;
@@ -153,7 +163,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
   int cus = 0;
   if ((s = device_cus(&cus)) != ATTN_OK) return s;
-  tattn::FwdArgs a{q, k, v, o, lse, B * H, N, d, scale, dtype == ATTN_FP32, stream, cus, env_waves()};
+  tattn::FwdArgs a{q, k, v, o, lse, B * H, N, d, scale, dtype == ATTN_FP32, stream, cus, env_waves(),
+                   env_int("TILED_ATTN_FWD_VPAD", {8, 16, 32})};
   const hipError_t e = tattn::launch_attn_fwd(a);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -21,211 +21,396 @@
 //     for O^T = V^T P^T (so V needs no transposing copy);
 //   * rows are padded by 16 bytes in LDS to spread banks;
 //   * the last key tile of a ragged N masks keys >= N (p = 0).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace tattn {
 
 // ---------------------------------------------------------------------------
-// bf16 forward
+// bf16 forward: shared pieces
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-struct FwdBf16Cfg {
-  static constexpr int R = 32;                 // query rows per wave
-  static constexpr int BM = R * NW;            // query rows per workgroup
-  static constexpr int BN = 64;                // keys per step
-  static constexpr int PITCH = D + 8;          // LDS row pitch (bf16 elements)
-  static constexpr int TILE = BN * PITCH;      // elements per staged K or V tile
-  static constexpr int THREADS = NW * 64;
-  static constexpr int CHUNKS = BN * D / 8;    // 16-byte chunks per K or V tile
-  static constexpr int CPT = CHUNKS / THREADS; // chunks per thread per tile
-  static constexpr int DK = D / 16;            // k-steps of the score product
-  static constexpr int DB = D / 32;            // 32-wide blocks of d
-  static_assert(CHUNKS % THREADS == 0, "tile must split evenly over the workgroup");
-  static constexpr size_t LDS_BYTES = 2 * 2 * TILE * sizeof(bf16);
+template <int D, int VPAD = 32>
+struct FwdTile {
+  static constexpr int BN = 64;                 // keys per step
+  static constexpr int KPITCH = D + 8;          // K row pitch (bf16): row stride = 4 banks mod 64
+  static constexpr int VPITCH = D + VPAD;       // V row pitch (bf16): the 4 rows of one
+                                                // transposed read land on disjoint banks
+  static constexpr int KTILE = BN * KPITCH;
+  static constexpr int VTILE = BN * VPITCH;
+  static constexpr int STAGE = KTILE + VTILE;   // one K tile followed by one V tile
+  static constexpr int DK = D / 16;             // k-steps of the score product
+  static constexpr int DB = D / 32;             // 32-wide blocks of d
 };
 
+// The running max is only moved when a tile's max exceeds it by more than
+// this (base-2 units): p = 2^(c s - m) then stays <= 2^8, exact in the fp32
+// sum and in the bf16 operand's exponent range, and the rescale of the
+// output accumulator (a multiply per accumulator element) is skipped for
+// almost every tile. The shift cancels in o / l, so the result is the same
+// softmax as with the running max itself.
+constexpr float kLazyRescale = 8.0f;
+
+// S^T = K Q^T for one 64-key tile whose rows sit at swap23(key) in `kt`.
+// sacc[kb][i] then holds key 32 kb + 16 (i/8) + 8 h + i%8 for this lane's query.
+template <int D>
+__device__ __forceinline__ void score_tile(const bf16* kt, const bf16x8* qf, int lq, int h,
+                                           f32x16* sacc) {
+  using T = FwdTile<D>;
+  f32x16 a0, a1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a0[i] = a1[i] = 0.f;
+  const bf16* k0 = kt + lq * T::KPITCH + 8 * h;
+  const bf16* k1 = k0 + 32 * T::KPITCH;
+#pragma unroll
+  for (int s = 0; s < T::DK; ++s) {
+    a0 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 16 * s)), qf[s], a0);
+    a1 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k1 + 16 * s)), qf[s], a1);
+  }
+  sacc[0] = a0;
+  sacc[1] = a1;
+}
+
+// Online softmax update (Lecture 17 page, §8.3) for the query this lane owns,
+// over one 64-key tile whose first key is key0. Produces P (bf16, packed in
+// the B-operand order of pv_tile), updates the running (m, l) and rescales
+// the output accumulator by alpha when the running max moves.
+template <bool RAGGED, int DB>
+__device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, int N, int h,
+                                             float& m_run, float& l_run, f32x16* oacc,
+                                             u32x4* pw) {
+  if (RAGGED) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7) >= N) sacc[kb][i] = -INFINITY;
+  }
+  float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+  mx = max_with_other_half(mx);
+  const float mt = mx * c;
+  const float m_new = mt > m_run + kLazyRescale ? mt : m_run;
+  const float alpha = fast_exp2(m_run - m_new);
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      float p0 = fast_exp2(fmaf(sacc[kb][i], c, -m_new));
+      float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_new));
+      if (RAGGED) {
+        p0 = sacc[kb][i] == -INFINITY ? 0.f : p0;
+        p1 = sacc[kb][i + 1] == -INFINITY ? 0.f : p1;
+      }
+      ls0 += p0;
+      ls1 += p1;
+      pw[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+    }
+  l_run = fmaf(alpha, l_run, ls0 + ls1);
+  m_run = m_new;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+  }
+}
+
+// O^T += V^T P^T for one 64-key tile (V rows in key order in `vt`), with V^T
+// read by ds_read_b64_tr_b16: step t covers keys 16 t + 8 h + 0..7.
+template <int D, int VPAD>
+__device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, int lane, int h,
+                                        f32x16* oacc) {
+  using T = FwdTile<D, VPAD>;
+  const int g = lane >> 4, j16 = lane & 15;
+  const bf16* vp = vt + (8 * h + (j16 >> 2)) * T::VPITCH + 16 * (g & 1) + 4 * (j16 & 3);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bf16x8 pf = as_bf16x8(pw[t]);
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const bf16x8 vf = lds_read_tr_pair(vp + 16 * t * T::VPITCH + 32 * db,
+                                         vp + (16 * t + 4) * T::VPITCH + 32 * db);
+      oacc[db] = mfma32x32x16(vf, pf, oacc[db]);
+    }
+  }
+}
+
+// One MFMA phase of the ping-pong schedule: O^T += V^T P^T for the current
+// tile interleaved with S^T = K Q^T for the next tile (independent chains,
+// so neither waits on the other's results).
+template <int D, int VPAD>
+__device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const bf16x8* qf,
+                                           const u32x4* pw, int lane, int lq, int h,
+                                           f32x16* sacc, f32x16* oacc) {
+  using T = FwdTile<D, VPAD>;
+  constexpr int SPT = T::DK / 4;  // score k-steps per 16-key step of the value product
+  const int g = lane >> 4, j16 = lane & 15;
+  const bf16* vp = vt + (8 * h + (j16 >> 2)) * T::VPITCH + 16 * (g & 1) + 4 * (j16 & 3);
+  const bf16* k0 = kt + lq * T::KPITCH + 8 * h;
+  const bf16* k1 = k0 + 32 * T::KPITCH;
+  f32x16 a0, a1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a0[i] = a1[i] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bf16x8 pf = as_bf16x8(pw[t]);
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const bf16x8 vf = lds_read_tr_pair(vp + 16 * t * T::VPITCH + 32 * db,
+                                         vp + (16 * t + 4) * T::VPITCH + 32 * db);
+      oacc[db] = mfma32x32x16(vf, pf, oacc[db]);
+    }
+#pragma unroll
+    for (int s = SPT * t; s < SPT * (t + 1); ++s) {
+      a0 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 16 * s)), qf[s], a0);
+      a1 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k1 + 16 * s)), qf[s], a1);
+    }
+  }
+  sacc[0] = a0;
+  sacc[1] = a1;
+}
+
+// Epilogue: O = o / l (bf16), LSE = ln 2 (m + log2 l).
+template <int D>
+__device__ __forceinline__ void store_output(const f32x16* oacc, float m_run, float l_run,
+                                             bf16* orow, float* lse, bool q_ok, int h) {
+  const float l_tot = add_other_half(l_run);
+  const float inv = 1.f / l_tot;
+  if (!q_ok) return;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[db][4 * r + 0] * inv, oacc[db][4 * r + 1] * inv);
+      w[1] = pack_bf16x2(oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv);
+      *(u32x2*)(orow + 32 * db + 8 * r + 4 * h) = w;
+    }
+  if (h == 0) *lse = (m_run + fast_log2(l_tot)) * kLn2;
+}
+
+// Q^T as the B operand: lane (query lq, half h) holds d = 16 s + 8 h .. +7.
+template <int D>
+__device__ __forceinline__ void load_q(const bf16* qrow, bool q_ok, int h, bf16x8* qf) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 x = {0, 0, 0, 0};
+    if (q_ok) x = *(const u32x4*)(qrow + 16 * s + 8 * h);
+    qf[s] = as_bf16x8(x);
+  }
+}
+
+// Rows [r0, r0 + ROWS) of a K tile and a V tile: global -> registers (zero
+// for keys >= N, with no memory access), then registers -> LDS.
+template <int D, int VPAD, int ROWS, int THREADS>
+struct TileRows {
+  static constexpr int CPT = ROWS * (D / 8) / THREADS;  // 16-byte chunks per thread per tensor
+  static_assert(ROWS * (D / 8) % THREADS == 0, "rows must split evenly over the threads");
+  u32x4 k[CPT], v[CPT];
+
+  __device__ __forceinline__ void load(const bf16* Kb, const bf16* Vb, int kt_k, int kt_v, int r0,
+                                       int N, int t) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = t + i * THREADS;
+      const int row = r0 + ch / (D / 8), col = (ch % (D / 8)) * 8;
+      const int kk = kt_k * 64 + row, kv = kt_v * 64 + row;
+      u32x4 zk = {0, 0, 0, 0}, zv = {0, 0, 0, 0};
+      if (kk < N) zk = *(const u32x4*)(Kb + (size_t)kk * D + col);
+      if (kv < N) zv = *(const u32x4*)(Vb + (size_t)kv * D + col);
+      k[i] = zk;
+      v[i] = zv;
+    }
+  }
+  __device__ __forceinline__ void store(bf16* kt, bf16* vt, int r0, int t) {
+    using T = FwdTile<D, VPAD>;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = t + i * THREADS;
+      const int row = r0 + ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *(u32x4*)(kt + swap23(row) * T::KPITCH + col) = k[i];
+      *(u32x4*)(vt + row * T::VPITCH + col) = v[i];
+    }
+  }
+};
+
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 forward, generic: NW waves in lock step, one barrier per key tile.
+// ---------------------------------------------------------------------------
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 2))) void attn_fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_tiles,
-    float c, int remap) {
-  using C = FwdBf16Cfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * C::TILE];
-  // stage b: K tile at smem + 2 b TILE, V tile right after it
-  auto ks = [&](int b) { return smem + 2 * b * C::TILE; };
-  auto vs = [&](int b) { return smem + (2 * b + 1) * C::TILE; };
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 2)))
+void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                          const bf16* __restrict__ V, bf16* __restrict__ O,
+                          float* __restrict__ LSE, int N, int n_qtiles, int total_tiles, float c,
+                          int remap) {
+  constexpr int VPAD = 32;
+  using T = FwdTile<D, VPAD>;
+  constexpr int BM = 32 * NW;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::STAGE];
+  auto ks = [&](int b) { return smem + b * T::STAGE; };
+  auto vs = [&](int b) { return smem + b * T::STAGE + T::KTILE; };
 
   const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * N * D;
-  const bf16* Qb = Q + base;
   const bf16* Kb = K + base;
   const bf16* Vb = V + base;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int lq = lane & 31;
-  const int h = lane >> 5;
-  const int q_row = qt * C::BM + wave * C::R + lq;   // the query this lane owns
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
 
-  // Q^T as the B operand: lane (query lq, half h) holds d = 16 s + 8 h .. +7.
-  bf16x8 qf[C::DK];
-#pragma unroll
-  for (int s = 0; s < C::DK; ++s) {
-    u32x4 x = {0, 0, 0, 0};
-    if (q_ok) x = *(const u32x4*)(Qb + (size_t)q_row * D + 16 * s + 8 * h);
-    qf[s] = as_bf16x8(x);
-  }
+  bf16x8 qf[T::DK];
+  load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
 
-  const int n_kt = (N + C::BN - 1) / C::BN;
-  u32x4 kreg[C::CPT], vreg[C::CPT];
-
-  auto load_tile = [&](int j) {
+  f32x16 oacc[T::DB];
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::THREADS;
-      const int row = ch / (D / 8);
-      const int col = (ch % (D / 8)) * 8;
-      const int key = j * C::BN + row;
-      u32x4 zk = {0, 0, 0, 0}, zv = {0, 0, 0, 0};
-      if (key < N) {
-        zk = *(const u32x4*)(Kb + (size_t)key * D + col);
-        zv = *(const u32x4*)(Vb + (size_t)key * D + col);
-      }
-      kreg[i] = zk;
-      vreg[i] = zv;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::THREADS;
-      const int row = ch / (D / 8);
-      const int col = (ch % (D / 8)) * 8;
-      *(u32x4*)(ks(buf) + swap23(row) * C::PITCH + col) = kreg[i];
-      *(u32x4*)(vs(buf) + row * C::PITCH + col) = vreg[i];
-    }
-  };
-
-  f32x16 oacc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;  // running max of c * s (base-2 domain)
-  float l_run = 0.f;        // running sum over this lane's half of the keys
+  float m_run = -INFINITY, l_run = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  const int n_kt = (N + T::BN - 1) / T::BN;
+  TileRows<D, VPAD, 64, NW * 64> st;
+  st.load(Kb, Vb, 0, 0, 0, N, tid);
+  st.store(ks(0), vs(0), 0, tid);
   __syncthreads();
-
-  // Lane-constant parts of the transposed V read (see device_common.h).
-  const int g = lane >> 4;
-  const int j16 = lane & 15;
-  const int v_col = 16 * (g & 1) + 4 * (j16 & 3);
-  const int v_row = 8 * h + (j16 >> 2);
 
   for (int j = 0; j < n_kt; ++j) {
     const int cur = j & 1;
-    if (j + 1 < n_kt) load_tile(j + 1);
-
-    // S^T = K Q^T for the 64 keys of this step: two 32-key blocks.
+    if (j + 1 < n_kt) st.load(Kb, Vb, j + 1, j + 1, 0, N, tid);
     f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const bf16* kp = ks(cur) + (32 * kb + lq) * C::PITCH + 8 * h;
-#pragma unroll
-      for (int s = 0; s < C::DK; ++s) {
-        bf16x8 kf = as_bf16x8(*(const u32x4*)(kp + 16 * s));
-        sacc[kb] = mfma32x32x16(kf, qf[s], sacc[kb]);
-      }
-    }
-
-    // Keys of this lane: key(kb, i) = j*64 + 32 kb + 16 (i/8) + 8 h + i%8.
-    const bool ragged = (j + 1) * C::BN > N;
-    if (ragged) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j * C::BN + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7);
-          if (key >= N) sacc[kb][i] = -INFINITY;
-        }
-    }
-
-    // Online softmax update for the query this lane owns.
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = max_with_other_half(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = fast_exp2(m_run - m_new);
-    float lsum = 0.f;
-    unsigned pk[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float p0 = fast_exp2(fmaf(sacc[kb][i], c, -m_new));
-        float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_new));
-        if (ragged) {
-          if (sacc[kb][i] == -INFINITY) p0 = 0.f;
-          if (sacc[kb][i + 1] == -INFINITY) p1 = 0.f;
-        }
-        lsum += p0 + p1;
-        pk[kb][i >> 1] = pack_bf16x2(p0, p1);
-      }
-    l_run = fmaf(alpha, l_run, lsum);
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-
-    // O^T += V^T P^T over the 4 steps of 16 keys.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 pw = {pk[t >> 1][4 * (t & 1) + 0], pk[t >> 1][4 * (t & 1) + 1],
-                  pk[t >> 1][4 * (t & 1) + 2], pk[t >> 1][4 * (t & 1) + 3]};
-      const bf16x8 pf = as_bf16x8(pw);
-      const bf16* vp = vs(cur) + (16 * t + v_row) * C::PITCH + v_col;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        bf16x8 vf = lds_read_tr_pair(vp + 32 * db, vp + 4 * C::PITCH + 32 * db);
-        oacc[db] = mfma32x32x16(vf, pf, oacc[db]);
-      }
-    }
-
-    if (j + 1 < n_kt) store_tile(cur ^ 1);
+    u32x4 pw[4];
+    score_tile<D>(ks(cur), qf, lq, h, sacc);
+    if ((j + 1) * T::BN > N)
+      softmax_tile<true, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
+    else
+      softmax_tile<false, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
+    pv_tile<D, VPAD>(vs(cur), pw, lane, h, oacc);
+    if (j + 1 < n_kt) st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
     __syncthreads();
   }
+  store_output<D>(oacc, m_run, l_run, O + base + (size_t)q_row * D, LSE + (size_t)bh * N + q_row,
+                  q_ok, h);
+}
 
-  // Epilogue: O = o / l, LSE = ln(2) (m + log2 l).
-  const float l_tot = add_other_half(l_run);
-  const float inv = 1.f / l_tot;
-  if (q_ok) {
-    bf16* orow = O + base + (size_t)q_row * D;
+// ---------------------------------------------------------------------------
+// bf16 forward, ping-pong: 8 waves in two groups of 4 (one wave of each group
+// per SIMD). Within a wave the work of one key tile is split into an MFMA
+// phase (S^T of tile j+1 and O^T += V^T P^T of tile j) and a VALU phase
+// (online softmax of tile j+1). Group B runs one phase behind group A, and
+// every phase ends at a workgroup barrier, so on each SIMD one wave feeds
+// the matrix core while the other wave computes exponentials: a wave's own
+// VALU work does not overlap its own MFMAs, but another wave's does.
+// K and V tiles are double-buffered; each group stages half of every tile
+// during its VALU phase (group A: K_{j+2}, V_{j+1}; group B, one phase later
+// in time but one tile ahead: K_{j+3}, V_{j+2}), which keeps each buffer
+// free until both groups have read it.
+// ---------------------------------------------------------------------------
+template <int D, int VPAD>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                   const bf16* __restrict__ V, bf16* __restrict__ O,
+                                   float* __restrict__ LSE, int N, int n_qtiles, int total_tiles,
+                                   float c, int remap) {
+  using T = FwdTile<D, VPAD>;
+  constexpr int BM = 256;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::STAGE];
+  auto ks = [&](int b) { return smem + (b & 1) * T::STAGE; };
+  auto vs = [&](int b) { return smem + (b & 1) * T::STAGE + T::KTILE; };
+
+  const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
+  const int bh = tile / n_qtiles;
+  const int qt = tile - bh * n_qtiles;
+  const size_t base = (size_t)bh * N * D;
+  const bf16* Kb = K + base;
+  const bf16* Vb = V + base;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int grp = wave >> 2;          // 0: group A, 1: group B
+  const int gtid = tid & 255;         // thread index within the group
+  const int r0 = 32 * grp;            // rows of each tile this group stages
+  const int q_row = qt * BM + wave * 32 + lq;
+  const bool q_ok = q_row < N;
+
+  bf16x8 qf[T::DK];
+  load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
+
+  f32x16 oacc[T::DB];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * r + 0] * inv, oacc[db][4 * r + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv);
-        *(u32x2*)(orow + 32 * db + 8 * r + 4 * h) = w;
-      }
-    if (h == 0) LSE[(size_t)bh * N + q_row] = (m_run + fast_log2(l_tot)) * kLn2;
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int n_kt = (N + T::BN - 1) / T::BN;
+  const bool ragged_tail = (N % T::BN) != 0;
+
+  {  // prologue: everyone stages K_0, V_0 and K_1
+    TileRows<D, VPAD, 64, 512> st0;
+    st0.load(Kb, Vb, 0, 0, 0, N, tid);
+    st0.store(ks(0), vs(0), 0, tid);
+    st0.load(Kb, Vb, 1, 1, 0, N, tid);
+    st0.store(ks(1), vs(1), 0, tid);  // V_1 rows are restaged below; K_1 is final
   }
+  __syncthreads();
+  if (grp == 1) phase_barrier();
+
+  f32x16 sacc[2];
+  u32x4 pw[4];
+  // Group A stages (K_{j+2}, V_{j+1}) in VALU phase j, group B (K_{j+3}, V_{j+2}).
+  // Tiles past the end are zero-filled without memory traffic into buffers
+  // no wave reads any more.
+  TileRows<D, VPAD, 32, 256> st;
+
+  score_tile<D>(ks(0), qf, lq, h, sacc);  // MFMA phase of tile 0
+  phase_barrier();
+  if (grp == 1) st.load(Kb, Vb, 2, 1, r0, N, gtid);  // VALU phase "j = -1"
+  if (n_kt == 1 && ragged_tail)
+    softmax_tile<true, T::DB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
+  else
+    softmax_tile<false, T::DB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
+  if (grp == 1) st.store(ks(2), vs(1), r0, gtid);
+  phase_barrier();
+
+  auto body = [&](auto ragged, int j) {
+    // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1.
+    mfma_phase<D, VPAD>(ks(j + 1), vs(j), qf, pw, lane, lq, h, sacc, oacc);
+    phase_barrier();
+    // VALU phase: online softmax of tile j+1, staging of later tiles.
+    const int tk = j + 2 + grp, tv = j + 1 + grp;
+    st.load(Kb, Vb, tk, tv, r0, N, gtid);
+    softmax_tile<decltype(ragged)::value, T::DB>(sacc, c, (j + 1) * T::BN, N, h, m_run, l_run,
+                                                 oacc, pw);
+    st.store(ks(tk), vs(tv), r0, gtid);
+    phase_barrier();
+  };
+  int j = 0;
+  for (; j + 2 < n_kt; ++j) body(std::false_type{}, j);
+  if (j + 1 < n_kt) {
+    if (ragged_tail)
+      body(std::true_type{}, j);
+    else
+      body(std::false_type{}, j);
+    ++j;
+  }
+  // last tile: value product only
+  pv_tile<D, VPAD>(vs(j), pw, lane, h, oacc);
+  phase_barrier();
+  phase_barrier();
+  if (grp == 0) phase_barrier();
+  store_output<D>(oacc, m_run, l_run, O + base + (size_t)q_row * D, LSE + (size_t)bh * N + q_row,
+                  q_ok, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,14 +529,25 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 static hipError_t launch_bf16(const FwdArgs& a) {
-  using C = FwdBf16Cfg<D, NW>;
-  const int n_qtiles = (int)((a.N + C::BM - 1) / C::BM);
+  constexpr int BM = 32 * NW;
+  const int n_qtiles = (int)((a.N + BM - 1) / BM);
   const int64_t total = (int64_t)a.BH * n_qtiles;
   if (total > INT32_MAX) return hipErrorInvalidValue;
   const int remap = (total % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)total), dim3(C::THREADS), 0,
-                     (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                     (bf16*)a.o, a.lse, (int)a.N, n_qtiles, (int)total, a.scale * kLog2e, remap);
+  if constexpr (NW == 8) {
+    auto kern = a.vpad == 16 ? attn_fwd_bf16_pingpong_kernel<D, 16>
+                             : a.vpad == 8 ? attn_fwd_bf16_pingpong_kernel<D, 8>
+                                           : attn_fwd_bf16_pingpong_kernel<D, 32>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(512), 0,
+                       (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, (bf16*)a.o, a.lse, (int)a.N, n_qtiles, (int)total,
+                       a.scale * kLog2e, remap);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0,
+                       (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, (bf16*)a.o, a.lse, (int)a.N, n_qtiles, (int)total,
+                       a.scale * kLog2e, remap);
+  }
   return hipGetLastError();
 }
 

@@ -60,12 +60,13 @@ __device__ __forceinline__ float add_other_half(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Round-to-nearest-even fp32 -> bf16 for a pair, packed low/high.
+typedef __bf16 bf16x2_ev __attribute__((ext_vector_type(2)));
+typedef float f32x2_ev __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 for a pair, packed low/high (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  bf16 a = (bf16)lo;
-  bf16 b = (bf16)hi;
-  return (unsigned)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+  const f32x2_ev f = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_ev));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
