@@ -86,8 +86,12 @@ def cpu_baseline(w, x, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The warm-up is long on purpose: under sustained load the MI355X raises
+    # its shader clock over tens of milliseconds (measured on this kernel:
+    # ~1.85 GHz after 10 launches, a steady ~2.05 GHz after ~100 ms), so a
+    # short warm-up times the clock ramp rather than the kernel.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward figures in 'extra'")

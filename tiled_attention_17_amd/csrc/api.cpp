@@ -163,8 +163,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
   int cus = 0;
   if ((s = device_cus(&cus)) != ATTN_OK) return s;
-  tattn::FwdArgs a{q, k, v, o, lse, B * H, N, d, scale, dtype == ATTN_FP32, stream, cus, env_waves(),
-                   env_int("TILED_ATTN_FWD_VPAD", {8, 16, 32})};
+  tattn::FwdArgs a{q, k, v, o, lse, B * H, N, d, scale, dtype == ATTN_FP32, stream, cus, env_waves()};
   const hipError_t e = tattn::launch_attn_fwd(a);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return ok();

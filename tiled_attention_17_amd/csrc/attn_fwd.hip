@@ -7,7 +7,7 @@
 // O = o / l at the end). Exponentials are taken in base 2 with
 // c = scale * log2(e) folded into one FMA: e^(scale s - m) = 2^(c s - m2).
 //
-// MI355X mapping (bf16 kernel):
+// MI355X mapping (bf16 kernels):
 //   * one workgroup = NW waves, each wave owns 32 query rows (BM = 32 NW);
 //   * the wave computes the TRANSPOSED score tile S^T = K Q^T on
 //     v_mfma_f32_32x32x16_bf16, so each lane owns one query column: the row
@@ -15,12 +15,22 @@
 //     scalars and need one cross-half exchange (v_permlane32_swap) per tile;
 //   * Q^T (the B operand) stays in VGPRs for the whole key sweep;
 //   * K and V tiles (64 keys) are staged through LDS, double-buffered, with
-//     16-byte coalesced global loads issued one tile ahead; K rows are placed
-//     at swap23(key) so the score accumulator is already in the operand order
-//     of the next product, and V is read transposed with ds_read_b64_tr_b16
-//     for O^T = V^T P^T (so V needs no transposing copy);
-//   * rows are padded by 16 bytes in LDS to spread banks;
-//   * the last key tile of a ragged N masks keys >= N (p = 0).
+//     16-byte coalesced global loads; K rows are placed at swap23(key) so the
+//     score accumulator is already in the operand order of the next product;
+//   * V is stored TRANSPOSED in LDS (V^T, one row of 64 keys per d), so the
+//     A operand of O^T += V^T P^T is one ds_read_b128 per MFMA. The
+//     transpose is done once per workgroup while staging: each lane loads the
+//     same 8 d-values of two adjacent keys, v_perm_b32 pairs the keys, and
+//     v_permlane32_swap / v_permlane16_swap exchange the pairs of 4 lanes
+//     (a 4 x 4 dword transpose), leaving each lane 8 consecutive keys of two
+//     d rows. (A ds_read_b64_tr_b16 of row-major V moves half the bytes per
+//     LDS instruction at a third of the b128 rate: the LDS, not the matrix
+//     core, then bounds the kernel.)
+//   * the 16-byte slots of a V^T row are XOR-swizzled by vt_swz(d) so that
+//     the MFMA operand reads are free of bank conflicts and the transposed
+//     writes at most two-way conflicted;
+//   * the last key tile of a ragged N masks keys >= N (p = 0) and stages
+//     zeros for them.
 #include <type_traits>
 
 #include "device_common.h"
@@ -31,18 +41,24 @@ namespace tattn {
 // ---------------------------------------------------------------------------
 // bf16 forward: shared pieces
 // ---------------------------------------------------------------------------
-template <int D, int VPAD = 32>
+template <int D>
 struct FwdTile {
-  static constexpr int BN = 64;                 // keys per step
-  static constexpr int KPITCH = D + 8;          // K row pitch (bf16): row stride = 4 banks mod 64
-  static constexpr int VPITCH = D + VPAD;       // V row pitch (bf16): the 4 rows of one
-                                                // transposed read land on disjoint banks
-  static constexpr int KTILE = BN * KPITCH;
-  static constexpr int VTILE = BN * VPITCH;
-  static constexpr int STAGE = KTILE + VTILE;   // one K tile followed by one V tile
-  static constexpr int DK = D / 16;             // k-steps of the score product
-  static constexpr int DB = D / 32;             // 32-wide blocks of d
+  static constexpr int BN = 64;              // keys per step
+  static constexpr int KPITCH = D + 8;       // K row pitch (bf16): row stride = 4 banks mod 64
+  static constexpr int KTILE = BN * KPITCH;  // K tile, bf16 elements
+  static constexpr int VTILE = D * BN;       // V^T tile: D rows of BN keys, no padding
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int DK = D / 16;          // k-steps of the score product
+  static constexpr int DB = D / 32;          // 32-wide blocks of d
+  static constexpr int CPR = D / 8;          // 16-byte chunks per K or V row
+  static constexpr int VKEYS = 128 / CPR;    // keys one wave transposes per pass
 };
+
+// XOR swizzle of the 8 sixteen-byte slots of V^T row d. Reads of one MFMA
+// operand touch 16 consecutive rows at one logical slot: (d & 1, vt_swz(d))
+// is then distinct across them (no conflict). The transposed writes touch
+// rows d = 8r + e (r = 0..15) at one slot: vt_swz takes each value twice.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
 
 // The running max is only moved when a tile's max exceeds it by more than
 // this (base-2 units): p = 2^(c s - m) then stays <= 2^8, exact in the fp32
@@ -51,6 +67,40 @@ struct FwdTile {
 // almost every tile. The shift cancels in o / l, so the result is the same
 // softmax as with the running max itself.
 constexpr float kLazyRescale = 8.0f;
+
+// Per-lane element offsets of the V^T operand reads: the A operand of step t,
+// d block db (rows d = 32 db + lq, keys 16 t + 8 h .. + 7) starts at
+// voff[t ^ db] + db * 32 * BN. With d = 32 db + lq, vt_swz(d) = f0 ^ 2 db for
+// f0 = vt_swz(lq), so the swizzled slot (2 t + h) ^ vt_swz(d) equals
+// (2 (t ^ db) + h) ^ f0: four per-lane offsets serve all sixteen reads.
+struct VtOffsets {
+  int o[4];
+  __device__ __forceinline__ VtOffsets(int lq, int h) {
+    const int f0 = vt_swz(lq);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = lq * 64 + 8 * ((2 * u + h) ^ f0);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 vt_read(const bf16* vt, const VtOffsets& vo, int t, int db) {
+  return as_bf16x8(*(const u32x4*)(vt + vo.o[t ^ db] + db * 32 * FwdTile<D>::BN));
+}
+
+// Issue order of a run of NMFMA MFMAs that each consume one LDS read: the
+// reads run LOOKAHEAD operands ahead of the MFMAs, one read per MFMA in
+// between (left alone, the scheduler hoists every read and runs out of
+// registers).
+template <int NMFMA, int LOOKAHEAD = 3>
+__device__ __forceinline__ void interleave_lds_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA - LOOKAHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
+}
 
 // S^T = K Q^T for one 64-key tile whose rows sit at swap23(key) in `kt`.
 // sacc[kb][i] then holds key 32 kb + 16 (i/8) + 8 h + i%8 for this lane's query.
@@ -68,14 +118,15 @@ __device__ __forceinline__ void score_tile(const bf16* kt, const bf16x8* qf, int
     a0 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 16 * s)), qf[s], a0);
     a1 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k1 + 16 * s)), qf[s], a1);
   }
+  interleave_lds_mfma<2 * T::DK>();
   sacc[0] = a0;
   sacc[1] = a1;
 }
 
 // Online softmax update (Lecture 17 page, §8.3) for the query this lane owns,
 // over one 64-key tile whose first key is key0. Produces P (bf16, packed in
-// the B-operand order of pv_tile), updates the running (m, l) and rescales
-// the output accumulator by alpha when the running max moves.
+// the B-operand order of the value product), updates the running (m, l) and
+// rescales the output accumulator by alpha when the running max moves.
 template <bool RAGGED, int DB>
 __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, int N, int h,
                                              float& m_run, float& l_run, f32x16* oacc,
@@ -121,37 +172,29 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
   }
 }
 
-// O^T += V^T P^T for one 64-key tile (V rows in key order in `vt`), with V^T
-// read by ds_read_b64_tr_b16: step t covers keys 16 t + 8 h + 0..7.
-template <int D, int VPAD>
-__device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, int lane, int h,
+// O^T += V^T P^T for one 64-key tile: step t covers keys 16 t + 8 h + 0..7.
+template <int D>
+__device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, const VtOffsets& vo,
                                         f32x16* oacc) {
-  using T = FwdTile<D, VPAD>;
-  const int g = lane >> 4, j16 = lane & 15;
-  const bf16* vp = vt + (8 * h + (j16 >> 2)) * T::VPITCH + 16 * (g & 1) + 4 * (j16 & 3);
+  using T = FwdTile<D>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const bf16x8 pf = as_bf16x8(pw[t]);
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
-      const bf16x8 vf = lds_read_tr_pair(vp + 16 * t * T::VPITCH + 32 * db,
-                                         vp + (16 * t + 4) * T::VPITCH + 32 * db);
-      oacc[db] = mfma32x32x16(vf, pf, oacc[db]);
-    }
+    for (int db = 0; db < T::DB; ++db) oacc[db] = mfma32x32x16(vt_read<D>(vt, vo, t, db), pf, oacc[db]);
   }
+  interleave_lds_mfma<4 * T::DB>();
 }
 
 // One MFMA phase of the ping-pong schedule: O^T += V^T P^T for the current
 // tile interleaved with S^T = K Q^T for the next tile (independent chains,
 // so neither waits on the other's results).
-template <int D, int VPAD>
+template <int D>
 __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const bf16x8* qf,
-                                           const u32x4* pw, int lane, int lq, int h,
+                                           const u32x4* pw, const VtOffsets& vo, int lq, int h,
                                            f32x16* sacc, f32x16* oacc) {
-  using T = FwdTile<D, VPAD>;
+  using T = FwdTile<D>;
   constexpr int SPT = T::DK / 4;  // score k-steps per 16-key step of the value product
-  const int g = lane >> 4, j16 = lane & 15;
-  const bf16* vp = vt + (8 * h + (j16 >> 2)) * T::VPITCH + 16 * (g & 1) + 4 * (j16 & 3);
   const bf16* k0 = kt + lq * T::KPITCH + 8 * h;
   const bf16* k1 = k0 + 32 * T::KPITCH;
   f32x16 a0, a1;
@@ -161,17 +204,14 @@ __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const
   for (int t = 0; t < 4; ++t) {
     const bf16x8 pf = as_bf16x8(pw[t]);
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
-      const bf16x8 vf = lds_read_tr_pair(vp + 16 * t * T::VPITCH + 32 * db,
-                                         vp + (16 * t + 4) * T::VPITCH + 32 * db);
-      oacc[db] = mfma32x32x16(vf, pf, oacc[db]);
-    }
+    for (int db = 0; db < T::DB; ++db) oacc[db] = mfma32x32x16(vt_read<D>(vt, vo, t, db), pf, oacc[db]);
 #pragma unroll
     for (int s = SPT * t; s < SPT * (t + 1); ++s) {
       a0 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 16 * s)), qf[s], a0);
       a1 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k1 + 16 * s)), qf[s], a1);
     }
   }
+  interleave_lds_mfma<4 * T::DB + 2 * T::DK>();
   sacc[0] = a0;
   sacc[1] = a1;
 }
@@ -206,36 +246,94 @@ __device__ __forceinline__ void load_q(const bf16* qrow, bool q_ok, int h, bf16x
   }
 }
 
-// Rows [r0, r0 + ROWS) of a K tile and a V tile: global -> registers (zero
-// for keys >= N, with no memory access), then registers -> LDS.
-template <int D, int VPAD, int ROWS, int THREADS>
-struct TileRows {
-  static constexpr int CPT = ROWS * (D / 8) / THREADS;  // 16-byte chunks per thread per tensor
-  static_assert(ROWS * (D / 8) % THREADS == 0, "rows must split evenly over the threads");
-  u32x4 k[CPT], v[CPT];
+// Transposes the two 16-byte V chunks this lane loaded (keys 2p, 2p+1 of a
+// pass, p = lane / 16, the same 8 d-values d0 .. d0+7) into two 16-byte V^T
+// pieces: 8 consecutive keys of rows d0 + 2p and d0 + 2p + 1.
+__device__ __forceinline__ void transpose_v_pair(u32x4 a, u32x4 b, u32x4& lo, u32x4& hi) {
+  unsigned c[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[2 * j] = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);      // (a.lo, b.lo): d = 2j
+    c[2 * j + 1] = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);  // (a.hi, b.hi): d = 2j + 1
+  }
+  // c[i] = key pair p of row d0 + i. Exchange over lane bit 5, then bit 4.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    auto r = __builtin_amdgcn_permlane32_swap(c[i], c[i + 4], false, false);
+    c[i] = r[0];
+    c[i + 4] = r[1];
+  }
+#pragma unroll
+  for (int i : {0, 1, 4, 5}) {
+    auto r = __builtin_amdgcn_permlane16_swap(c[i], c[i + 2], false, false);
+    c[i] = r[0];
+    c[i + 2] = r[1];
+  }
+  // Now c[2u] / c[2u+1] = key pair u of rows d0 + 2p / d0 + 2p + 1.
+  lo = (u32x4){c[0], c[2], c[4], c[6]};
+  hi = (u32x4){c[1], c[3], c[5], c[7]};
+}
+
+// Rows [r0, r0 + ROWS) of a K tile and of a V^T tile, staged by THREADS
+// threads: global -> registers (zero for keys >= N, with no memory access),
+// then registers -> LDS. K chunks are spread over all threads; V is staged
+// in passes of VKEYS keys per wave (each lane: two 16-byte loads).
+template <int D, int ROWS, int THREADS>
+struct Stager {
+  using T = FwdTile<D>;
+  static constexpr int WAVES = THREADS / 64;
+  static constexpr int KCPT = ROWS * T::CPR / THREADS;  // K chunks per thread
+  static constexpr int VPASS = ROWS / T::VKEYS;          // V passes in total
+  static constexpr int VPW = (VPASS + WAVES - 1) / WAVES;
+  static_assert(ROWS * T::CPR % THREADS == 0, "K rows must split evenly over the threads");
+  static_assert(ROWS % T::VKEYS == 0, "V rows must split into whole passes");
+  u32x4 k[KCPT], va[VPW], vb[VPW];
 
   __device__ __forceinline__ void load(const bf16* Kb, const bf16* Vb, int kt_k, int kt_v, int r0,
                                        int N, int t) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < KCPT; ++i) {
       const int ch = t + i * THREADS;
-      const int row = r0 + ch / (D / 8), col = (ch % (D / 8)) * 8;
-      const int kk = kt_k * 64 + row, kv = kt_v * 64 + row;
-      u32x4 zk = {0, 0, 0, 0}, zv = {0, 0, 0, 0};
-      if (kk < N) zk = *(const u32x4*)(Kb + (size_t)kk * D + col);
-      if (kv < N) zv = *(const u32x4*)(Vb + (size_t)kv * D + col);
-      k[i] = zk;
-      v[i] = zv;
+      const int row = r0 + ch / T::CPR, col = (ch % T::CPR) * 8;
+      const int kk = kt_k * T::BN + row;
+      u32x4 z = {0, 0, 0, 0};
+      if (kk < N) z = *(const u32x4*)(Kb + (size_t)kk * D + col);
+      k[i] = z;
+    }
+    const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
+    const int col = 8 * (r % T::CPR), g = r / T::CPR;
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      const int pass = wave + i * WAVES;
+      if (VPASS % WAVES == 0 || pass < VPASS) {
+        const int kv = kt_v * T::BN + r0 + pass * T::VKEYS + 8 * g + 2 * p;
+        u32x4 za = {0, 0, 0, 0}, zb = {0, 0, 0, 0};
+        if (kv < N) za = *(const u32x4*)(Vb + (size_t)kv * D + col);
+        if (kv + 1 < N) zb = *(const u32x4*)(Vb + (size_t)(kv + 1) * D + col);
+        va[i] = za;
+        vb[i] = zb;
+      }
     }
   }
   __device__ __forceinline__ void store(bf16* kt, bf16* vt, int r0, int t) {
-    using T = FwdTile<D, VPAD>;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < KCPT; ++i) {
       const int ch = t + i * THREADS;
-      const int row = r0 + ch / (D / 8), col = (ch % (D / 8)) * 8;
+      const int row = r0 + ch / T::CPR, col = (ch % T::CPR) * 8;
       *(u32x4*)(kt + swap23(row) * T::KPITCH + col) = k[i];
-      *(u32x4*)(vt + row * T::VPITCH + col) = v[i];
+    }
+    const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
+    const int d0 = 8 * (r % T::CPR) + 2 * p, g = r / T::CPR;
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      const int pass = wave + i * WAVES;
+      if (VPASS % WAVES == 0 || pass < VPASS) {
+        u32x4 lo, hi;
+        transpose_v_pair(va[i], vb[i], lo, hi);
+        const int slot = (r0 + pass * T::VKEYS) / 8 + g;
+        *(u32x4*)(vt + d0 * T::BN + 8 * (slot ^ vt_swz(d0))) = lo;
+        *(u32x4*)(vt + (d0 + 1) * T::BN + 8 * (slot ^ vt_swz(d0 + 1))) = hi;
+      }
     }
   }
 };
@@ -255,8 +353,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
                           const bf16* __restrict__ V, bf16* __restrict__ O,
                           float* __restrict__ LSE, int N, int n_qtiles, int total_tiles, float c,
                           int remap) {
-  constexpr int VPAD = 32;
-  using T = FwdTile<D, VPAD>;
+  using T = FwdTile<D>;
   constexpr int BM = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::STAGE];
   auto ks = [&](int b) { return smem + b * T::STAGE; };
@@ -271,6 +368,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
+  const VtOffsets vo(lq, h);
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
@@ -283,14 +381,21 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   float m_run = -INFINITY, l_run = 0.f;
 
   const int n_kt = (N + T::BN - 1) / T::BN;
-  TileRows<D, VPAD, 64, NW * 64> st;
-  st.load(Kb, Vb, 0, 0, 0, N, tid);
-  st.store(ks(0), vs(0), 0, tid);
+  // The next tile is staged in two halves of 32 rows (the first half's
+  // loads overlap the score product and softmax, the second half's the
+  // value product), which halves the staging registers.
+  Stager<D, 32, NW * 64> st;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    st.load(Kb, Vb, 0, 0, 32 * half, N, tid);
+    st.store(ks(0), vs(0), 32 * half, tid);
+  }
   __syncthreads();
 
   for (int j = 0; j < n_kt; ++j) {
     const int cur = j & 1;
-    if (j + 1 < n_kt) st.load(Kb, Vb, j + 1, j + 1, 0, N, tid);
+    const bool more = j + 1 < n_kt;
+    if (more) st.load(Kb, Vb, j + 1, j + 1, 0, N, tid);
     f32x16 sacc[2];
     u32x4 pw[4];
     score_tile<D>(ks(cur), qf, lq, h, sacc);
@@ -298,8 +403,12 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
       softmax_tile<true, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
     else
       softmax_tile<false, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
-    pv_tile<D, VPAD>(vs(cur), pw, lane, h, oacc);
-    if (j + 1 < n_kt) st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
+    if (more) {
+      st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
+      st.load(Kb, Vb, j + 1, j + 1, 32, N, tid);
+    }
+    pv_tile<D>(vs(cur), pw, vo, oacc);
+    if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 32, tid);
     __syncthreads();
   }
   store_output<D>(oacc, m_run, l_run, O + base + (size_t)q_row * D, LSE + (size_t)bh * N + q_row,
@@ -319,13 +428,13 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 // in time but one tile ahead: K_{j+3}, V_{j+2}), which keeps each buffer
 // free until both groups have read it.
 // ---------------------------------------------------------------------------
-template <int D, int VPAD>
+template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                    const bf16* __restrict__ V, bf16* __restrict__ O,
                                    float* __restrict__ LSE, int N, int n_qtiles, int total_tiles,
                                    float c, int remap) {
-  using T = FwdTile<D, VPAD>;
+  using T = FwdTile<D>;
   constexpr int BM = 256;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::STAGE];
   auto ks = [&](int b) { return smem + (b & 1) * T::STAGE; };
@@ -343,6 +452,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   const int r0 = 32 * grp;            // rows of each tile this group stages
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
+  const VtOffsets vo(lq, h);
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
@@ -357,7 +467,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   const bool ragged_tail = (N % T::BN) != 0;
 
   {  // prologue: everyone stages K_0, V_0 and K_1
-    TileRows<D, VPAD, 64, 512> st0;
+    Stager<D, 64, 512> st0;
     st0.load(Kb, Vb, 0, 0, 0, N, tid);
     st0.store(ks(0), vs(0), 0, tid);
     st0.load(Kb, Vb, 1, 1, 0, N, tid);
@@ -371,7 +481,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   // Group A stages (K_{j+2}, V_{j+1}) in VALU phase j, group B (K_{j+3}, V_{j+2}).
   // Tiles past the end are zero-filled without memory traffic into buffers
   // no wave reads any more.
-  TileRows<D, VPAD, 32, 256> st;
+  Stager<D, 32, 256> st;
 
   score_tile<D>(ks(0), qf, lq, h, sacc);  // MFMA phase of tile 0
   phase_barrier();
@@ -385,7 +495,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
 
   auto body = [&](auto ragged, int j) {
     // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1.
-    mfma_phase<D, VPAD>(ks(j + 1), vs(j), qf, pw, lane, lq, h, sacc, oacc);
+    mfma_phase<D>(ks(j + 1), vs(j), qf, pw, vo, lq, h, sacc, oacc);
     phase_barrier();
     // VALU phase: online softmax of tile j+1, staging of later tiles.
     const int tk = j + 2 + grp, tv = j + 1 + grp;
@@ -395,17 +505,18 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
     st.store(ks(tk), vs(tv), r0, gtid);
     phase_barrier();
   };
+  // bodies j = 0 .. n_kt - 2; only the one that takes the softmax of a
+  // ragged last tile masks keys.
+  const int n_body = n_kt - 1;
+  const int n_plain = ragged_tail ? n_body - 1 : n_body;
   int j = 0;
-  for (; j + 2 < n_kt; ++j) body(std::false_type{}, j);
-  if (j + 1 < n_kt) {
-    if (ragged_tail)
-      body(std::true_type{}, j);
-    else
-      body(std::false_type{}, j);
+  for (; j < n_plain; ++j) body(std::false_type{}, j);
+  if (j < n_body) {
+    body(std::true_type{}, j);
     ++j;
   }
   // last tile: value product only
-  pv_tile<D, VPAD>(vs(j), pw, lane, h, oacc);
+  pv_tile<D>(vs(j), pw, vo, oacc);
   phase_barrier();
   phase_barrier();
   if (grp == 0) phase_barrier();
@@ -535,10 +646,7 @@ static hipError_t launch_bf16(const FwdArgs& a) {
   if (total > INT32_MAX) return hipErrorInvalidValue;
   const int remap = (total % 8 == 0) ? 1 : 0;
   if constexpr (NW == 8) {
-    auto kern = a.vpad == 16 ? attn_fwd_bf16_pingpong_kernel<D, 16>
-                             : a.vpad == 8 ? attn_fwd_bf16_pingpong_kernel<D, 8>
-                                           : attn_fwd_bf16_pingpong_kernel<D, 32>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(512), 0,
+    hipLaunchKernelGGL((attn_fwd_bf16_pingpong_kernel<D>), dim3((unsigned)total), dim3(512), 0,
                        (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (bf16*)a.o, a.lse, (int)a.N, n_qtiles, (int)total,
                        a.scale * kLog2e, remap);

@@ -20,7 +20,6 @@ struct FwdArgs {
   void* stream;
   int num_cus;      // compute units of the device (grid sizing)
   int waves;        // 0 = choose; else waves per workgroup of the bf16 kernel (2, 4 or 8)
-  int vpad;         // 0 = default; else V row padding in bf16 elements (8, 16 or 32)
 };
 
 struct BwdArgs {
