@@ -17,7 +17,8 @@
  * (d innermost, no strides); LSE is a dense [B, H, N] float array. Every
  * pointer is a device pointer. Q, K and V share N (self-attention shape).
  *
- * Supported: d in {64, 128}; N >= 1 (any N; a ragged last tile is masked);
+ * Supported: d in {64, 128}; 1 <= N with N * d * 4 < 2^31 (one head is
+ * addressed with 32-bit byte offsets; any N, a ragged last tile is masked);
  * element type bfloat16 (ATTN_BF16; inputs and outputs bf16, all softmax
  * arithmetic and accumulation in fp32) or float (ATTN_FP32; fp32 everywhere,
  * forward only); scale finite and >= 0. A call with B*H*N == 0 does nothing

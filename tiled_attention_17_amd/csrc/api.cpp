@@ -56,8 +56,10 @@ attn_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype d
   if (d != 64 && d != 128)
     return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%lld is not supported (64 or 128)",
                 (long long)d);
-  if (N > (int64_t(1) << 30))
-    return fail(ATTN_ERR_UNSUPPORTED, "sequence length N=%lld exceeds 2^30", (long long)N);
+  // One head's [N, d] slice is addressed with 32-bit byte offsets.
+  if (N > INT32_MAX / (d * 4))
+    return fail(ATTN_ERR_UNSUPPORTED, "sequence length N=%lld too large for d=%lld (N*d*4 must be < 2^31)",
+                (long long)N, (long long)d);
   if (B > (int64_t(1) << 30) || H > (int64_t(1) << 30) || (B && H && B * H > (int64_t(1) << 31)))
     return fail(ATTN_ERR_UNSUPPORTED, "B*H too large (B=%lld H=%lld)", (long long)B, (long long)H);
   const int64_t bh = B * H;

@@ -60,6 +60,17 @@ struct FwdTile {
 // rows d = 8r + e (r = 0..15) at one slot: vt_swz takes each value twice.
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
 
+// Buffer resource over one head's [N, D] K or V slice. A load whose byte
+// offset is at or past N * D * 2 returns zeros without touching memory,
+// which is how rows >= N of a ragged last tile are staged (no branches).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16* base, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, N * D * 2, kBufferRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // The running max is only moved when a tile's max exceeds it by more than
 // this (base-2 units): p = 2^(c s - m) then stays <= 2^8, exact in the fp32
 // sum and in the bf16 operand's exponent range, and the rescale of the
@@ -147,6 +158,8 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
   const float mt = mx * c;
   const float m_new = mt > m_run + kLazyRescale ? mt : m_run;
   const float alpha = fast_exp2(m_run - m_new);
+  // The row sum adds the fp32 p (the sum of the bf16-rounded operands would
+  // put up to 2^-9 relative error into LSE when a few keys dominate a row).
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -275,7 +288,7 @@ __device__ __forceinline__ void transpose_v_pair(u32x4 a, u32x4 b, u32x4& lo, u3
 }
 
 // Rows [r0, r0 + ROWS) of a K tile and of a V^T tile, staged by THREADS
-// threads: global -> registers (zero for keys >= N, with no memory access),
+// threads: global -> registers (buffer loads: rows >= N read as zeros),
 // then registers -> LDS. K chunks are spread over all threads; V is staged
 // in passes of VKEYS keys per wave (each lane: two 16-byte loads).
 template <int D, int ROWS, int THREADS>
@@ -289,16 +302,13 @@ struct Stager {
   static_assert(ROWS % T::VKEYS == 0, "V rows must split into whole passes");
   u32x4 k[KCPT], va[VPW], vb[VPW];
 
-  __device__ __forceinline__ void load(const bf16* Kb, const bf16* Vb, int kt_k, int kt_v, int r0,
-                                       int N, int t) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                       int kt_k, int kt_v, int r0, int t) {
 #pragma unroll
     for (int i = 0; i < KCPT; ++i) {
       const int ch = t + i * THREADS;
       const int row = r0 + ch / T::CPR, col = (ch % T::CPR) * 8;
-      const int kk = kt_k * T::BN + row;
-      u32x4 z = {0, 0, 0, 0};
-      if (kk < N) z = *(const u32x4*)(Kb + (size_t)kk * D + col);
-      k[i] = z;
+      k[i] = buffer_load16(kr, ((kt_k * T::BN + row) * D + col) * 2);
     }
     const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
     const int col = 8 * (r % T::CPR), g = r / T::CPR;
@@ -307,11 +317,8 @@ struct Stager {
       const int pass = wave + i * WAVES;
       if (VPASS % WAVES == 0 || pass < VPASS) {
         const int kv = kt_v * T::BN + r0 + pass * T::VKEYS + 8 * g + 2 * p;
-        u32x4 za = {0, 0, 0, 0}, zb = {0, 0, 0, 0};
-        if (kv < N) za = *(const u32x4*)(Vb + (size_t)kv * D + col);
-        if (kv + 1 < N) zb = *(const u32x4*)(Vb + (size_t)(kv + 1) * D + col);
-        va[i] = za;
-        vb[i] = zb;
+        va[i] = buffer_load16(vr, (kv * D + col) * 2);
+        vb[i] = buffer_load16(vr, ((kv + 1) * D + col) * 2);
       }
     }
   }
@@ -363,8 +370,8 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * N * D;
-  const bf16* Kb = K + base;
-  const bf16* Vb = V + base;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(K + base, N);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<D>(V + base, N);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
@@ -387,7 +394,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   Stager<D, 32, NW * 64> st;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    st.load(Kb, Vb, 0, 0, 32 * half, N, tid);
+    st.load(krs, vrs, 0, 0, 32 * half, tid);
     st.store(ks(0), vs(0), 32 * half, tid);
   }
   __syncthreads();
@@ -395,7 +402,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   for (int j = 0; j < n_kt; ++j) {
     const int cur = j & 1;
     const bool more = j + 1 < n_kt;
-    if (more) st.load(Kb, Vb, j + 1, j + 1, 0, N, tid);
+    if (more) st.load(krs, vrs, j + 1, j + 1, 0, tid);
     f32x16 sacc[2];
     u32x4 pw[4];
     score_tile<D>(ks(cur), qf, lq, h, sacc);
@@ -405,7 +412,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
       softmax_tile<false, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
     if (more) {
       st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
-      st.load(Kb, Vb, j + 1, j + 1, 32, N, tid);
+      st.load(krs, vrs, j + 1, j + 1, 32, tid);
     }
     pv_tile<D>(vs(cur), pw, vo, oacc);
     if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 32, tid);
@@ -444,8 +451,8 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * N * D;
-  const bf16* Kb = K + base;
-  const bf16* Vb = V + base;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(K + base, N);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<D>(V + base, N);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int grp = wave >> 2;          // 0: group A, 1: group B
   const int gtid = tid & 255;         // thread index within the group
@@ -468,9 +475,9 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
 
   {  // prologue: everyone stages K_0, V_0 and K_1
     Stager<D, 64, 512> st0;
-    st0.load(Kb, Vb, 0, 0, 0, N, tid);
+    st0.load(krs, vrs, 0, 0, 0, tid);
     st0.store(ks(0), vs(0), 0, tid);
-    st0.load(Kb, Vb, 1, 1, 0, N, tid);
+    st0.load(krs, vrs, 1, 1, 0, tid);
     st0.store(ks(1), vs(1), 0, tid);  // V_1 rows are restaged below; K_1 is final
   }
   __syncthreads();
@@ -485,7 +492,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
 
   score_tile<D>(ks(0), qf, lq, h, sacc);  // MFMA phase of tile 0
   phase_barrier();
-  if (grp == 1) st.load(Kb, Vb, 2, 1, r0, N, gtid);  // VALU phase "j = -1"
+  if (grp == 1) st.load(krs, vrs, 2, 1, r0, gtid);  // VALU phase "j = -1"
   if (n_kt == 1 && ragged_tail)
     softmax_tile<true, T::DB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
   else
@@ -494,12 +501,14 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   phase_barrier();
 
   auto body = [&](auto ragged, int j) {
-    // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1.
+    // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1. The global
+    // loads of this group's share of later tiles are issued here, a phase
+    // before they are written to LDS, so their latency is hidden.
+    const int tk = j + 2 + grp, tv = j + 1 + grp;
+    st.load(krs, vrs, tk, tv, r0, gtid);
     mfma_phase<D>(ks(j + 1), vs(j), qf, pw, vo, lq, h, sacc, oacc);
     phase_barrier();
     // VALU phase: online softmax of tile j+1, staging of later tiles.
-    const int tk = j + 2 + grp, tv = j + 1 + grp;
-    st.load(Kb, Vb, tk, tv, r0, N, gtid);
     softmax_tile<decltype(ragged)::value, T::DB>(sacc, c, (j + 1) * T::BN, N, h, m_run, l_run,
                                                  oacc, pw);
     st.store(ks(tk), vs(tv), r0, gtid);

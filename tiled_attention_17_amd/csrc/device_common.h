@@ -71,6 +71,10 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Word 3 of a gfx9 buffer resource for raw (unformatted, stride 0) loads with
+// the range check against num_records enabled.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // 8 bf16 from two transposed 4-element LDS reads (see the header comment).
 __device__ __forceinline__ bf16x8 lds_read_tr_pair(const bf16* p0, const bf16* p1) {
   i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
