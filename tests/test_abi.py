@@ -84,7 +84,7 @@ def _err():
     (dict(o=A), 1, "overlaps input q"),
     (dict(o=A + 2 * T + 64), 1, "overlaps input v"),
     (dict(lse=A + 3 * T + 16), 1, "outputs o and lse overlap"),
-    (dict(N=(1 << 22) + 1), 2, "too large"),
+    (dict(N=(1 << 23) + 1), 2, "too large"),
 ])
 def test_fwd_rejects(kw, status, needle):
     assert _fwd(**kw) == status
