@@ -101,9 +101,12 @@ __device__ __forceinline__ bf16x8 vt_read(const bf16* vt, const VtOffsets& vo, i
 // Issue order of a run of NMFMA MFMAs that each consume one LDS read: the
 // reads run LOOKAHEAD operands ahead of the MFMAs, one read per MFMA in
 // between (left alone, the scheduler hoists every read and runs out of
-// registers).
-template <int NMFMA, int LOOKAHEAD = 3>
+// registers). NVMEM global loads of the same region go first (left alone,
+// the scheduler sinks them to the end of the region, which wastes the
+// latency they were issued early to hide).
+template <int NMFMA, int LOOKAHEAD = 3, int NVMEM = 0>
 __device__ __forceinline__ void interleave_lds_mfma() {
+  if (NVMEM > 0) __builtin_amdgcn_sched_group_barrier(0x020, NVMEM, 0);  // global loads first
   __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
 #pragma unroll
   for (int i = 0; i < NMFMA - LOOKAHEAD; ++i) {
@@ -202,7 +205,7 @@ __device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, const V
 // One MFMA phase of the ping-pong schedule: O^T += V^T P^T for the current
 // tile interleaved with S^T = K Q^T for the next tile (independent chains,
 // so neither waits on the other's results).
-template <int D>
+template <int D, int NVMEM = 0>
 __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const bf16x8* qf,
                                            const u32x4* pw, const VtOffsets& vo, int lq, int h,
                                            f32x16* sacc, f32x16* oacc) {
@@ -224,7 +227,7 @@ __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const
       a1 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k1 + 16 * s)), qf[s], a1);
     }
   }
-  interleave_lds_mfma<4 * T::DB + 2 * T::DK>();
+  interleave_lds_mfma<4 * T::DB + 2 * T::DK, 3, NVMEM>();
   sacc[0] = a0;
   sacc[1] = a1;
 }
@@ -506,7 +509,8 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
     // before they are written to LDS, so their latency is hidden.
     const int tk = j + 2 + grp, tv = j + 1 + grp;
     st.load(krs, vrs, tk, tv, r0, gtid);
-    mfma_phase<D>(ks(j + 1), vs(j), qf, pw, vo, lq, h, sacc, oacc);
+    mfma_phase<D, Stager<D, 32, 256>::KCPT + (Stager<D, 32, 256>::VPASS % 4 == 0 ? 2 : 0)>(
+        ks(j + 1), vs(j), qf, pw, vo, lq, h, sacc, oacc);
     phase_barrier();
     // VALU phase: online softmax of tile j+1, staging of later tiles.
     softmax_tile<decltype(ragged)::value, T::DB>(sacc, c, (j + 1) * T::BN, N, h, m_run, l_run,
