@@ -41,9 +41,11 @@ namespace tattn {
 // ---------------------------------------------------------------------------
 // bf16 forward: shared pieces
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int BN_ = 64>
 struct FwdTile {
-  static constexpr int BN = 64;              // keys per step
+  static constexpr int BN = BN_;             // keys per step (64 or 128)
+  static constexpr int NKB = BN / 32;        // 32-key blocks of a score tile
+  static constexpr int NT = BN / 16;         // 16-key steps of the value product
   static constexpr int KPITCH = D + 8;       // K row pitch (bf16): row stride = 4 banks mod 64
   static constexpr int KTILE = BN * KPITCH;  // K tile, bf16 elements
   static constexpr int VTILE = D * BN;       // V^T tile: D rows of BN keys, no padding
@@ -54,11 +56,20 @@ struct FwdTile {
   static constexpr int VKEYS = 128 / CPR;    // keys one wave transposes per pass
 };
 
-// XOR swizzle of the 8 sixteen-byte slots of V^T row d. Reads of one MFMA
-// operand touch 16 consecutive rows at one logical slot: (d & 1, vt_swz(d))
-// is then distinct across them (no conflict). The transposed writes touch
-// rows d = 8r + e (r = 0..15) at one slot: vt_swz takes each value twice.
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
+// XOR swizzle of the 16-byte slots of V^T row d (BN / 8 slots per row).
+// Reads of one MFMA operand touch 16 consecutive rows at one logical slot;
+// the transposed writes touch rows d = 8r + e (r = 0..15) at one slot.
+//   BN = 64 (128-byte rows, two per bank period): (d & 1, vt_swz(d)) is
+//     distinct over 16 consecutive rows (no read conflict); vt_swz takes
+//     each value twice over the written rows (two-way write conflict).
+//   BN = 128 (256-byte rows): vt_swz is a bijection over 16 consecutive
+//     rows and over the written rows (no conflict either way).
+// In both, vt_swz(32 b + x) = vt_swz(x) ^ 2 b for x < 32, b < 4.
+template <int BN>
+__device__ __forceinline__ int vt_swz(int d) {
+  if constexpr (BN == 64) return ((d >> 1) ^ (d >> 4)) & 7;
+  else return (d ^ (d >> 4)) & 15;
+}
 
 // Buffer resource over one head's [N, D] K or V slice. A load whose byte
 // offset is at or past N * D * 2 returns zeros without touching memory,
@@ -81,21 +92,22 @@ constexpr float kLazyRescale = 8.0f;
 
 // Per-lane element offsets of the V^T operand reads: the A operand of step t,
 // d block db (rows d = 32 db + lq, keys 16 t + 8 h .. + 7) starts at
-// voff[t ^ db] + db * 32 * BN. With d = 32 db + lq, vt_swz(d) = f0 ^ 2 db for
+// o[t ^ db] + db * 32 * BN. With d = 32 db + lq, vt_swz(d) = f0 ^ 2 db for
 // f0 = vt_swz(lq), so the swizzled slot (2 t + h) ^ vt_swz(d) equals
-// (2 (t ^ db) + h) ^ f0: four per-lane offsets serve all sixteen reads.
+// (2 (t ^ db) + h) ^ f0: BN / 16 per-lane offsets serve every read.
+template <int BN>
 struct VtOffsets {
-  int o[4];
+  int o[BN / 16];
   __device__ __forceinline__ VtOffsets(int lq, int h) {
-    const int f0 = vt_swz(lq);
+    const int f0 = vt_swz<BN>(lq);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = lq * 64 + 8 * ((2 * u + h) ^ f0);
+    for (int u = 0; u < BN / 16; ++u) o[u] = lq * BN + 8 * ((2 * u + h) ^ f0);
   }
 };
 
-template <int D>
-__device__ __forceinline__ bf16x8 vt_read(const bf16* vt, const VtOffsets& vo, int t, int db) {
-  return as_bf16x8(*(const u32x4*)(vt + vo.o[t ^ db] + db * 32 * FwdTile<D>::BN));
+template <int BN>
+__device__ __forceinline__ bf16x8 vt_read(const bf16* vt, const VtOffsets<BN>& vo, int t, int db) {
+  return as_bf16x8(*(const u32x4*)(vt + vo.o[t ^ db] + db * 32 * BN));
 }
 
 // Issue order of a run of NMFMA MFMAs that each consume one LDS read: the
@@ -141,22 +153,22 @@ __device__ __forceinline__ void score_tile(const bf16* kt, const bf16x8* qf, int
 // over one 64-key tile whose first key is key0. Produces P (bf16, packed in
 // the B-operand order of the value product), updates the running (m, l) and
 // rescales the output accumulator by alpha when the running max moves.
-template <bool RAGGED, int DB>
+template <bool RAGGED, int DB, int NKB = 2>
 __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, int N, int h,
                                              float& m_run, float& l_run, f32x16* oacc,
                                              u32x4* pw) {
   if (RAGGED) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (key0 + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7) >= N) sacc[kb][i] = -INFINITY;
   }
   float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    for (int i = (kb < 2 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
   mx = max_with_other_half(mx);
   const float mt = mx * c;
   const float m_new = mt > m_run + kLazyRescale ? mt : m_run;
@@ -165,7 +177,7 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
   // put up to 2^-9 relative error into LSE when a few keys dominate a row).
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       float p0 = fast_exp2(fmaf(sacc[kb][i], c, -m_new));
@@ -190,46 +202,86 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
 
 // O^T += V^T P^T for one 64-key tile: step t covers keys 16 t + 8 h + 0..7.
 template <int D>
-__device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, const VtOffsets& vo,
+__device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, const VtOffsets<64>& vo,
                                         f32x16* oacc) {
   using T = FwdTile<D>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const bf16x8 pf = as_bf16x8(pw[t]);
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) oacc[db] = mfma32x32x16(vt_read<D>(vt, vo, t, db), pf, oacc[db]);
+    for (int db = 0; db < T::DB; ++db) oacc[db] = mfma32x32x16(vt_read<64>(vt, vo, t, db), pf, oacc[db]);
   }
   interleave_lds_mfma<4 * T::DB>();
 }
 
+// Value-product steps of an MFMA phase in issue order: the keys of the
+// tile's second half (steps t = NT/2 .. NT-1) first -- their V^T columns were
+// staged by the other group a full phase before the phase starts, so the
+// first operands can be read before the phase's barrier -- then the first
+// half (t = 0 .. NT/2-1).
+template <int NT>
+__device__ __forceinline__ constexpr int pv_step_t(int k, int db_count) {
+  return (k / db_count + NT / 2) % NT;
+}
+constexpr int kPrefetch = 3;  // V^T operand reads issued before the barrier
+
+// First kPrefetch V^T operands of the next MFMA phase (see pv_step_t).
+template <int D, int BN>
+__device__ __forceinline__ void prefetch_pv(const bf16* vt, const VtOffsets<BN>& vo, bf16x8* pre) {
+  using T = FwdTile<D, BN>;
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) pre[k] = vt_read<BN>(vt, vo, pv_step_t<T::NT>(k, T::DB), k % T::DB);
+}
+
 // One MFMA phase of the ping-pong schedule: O^T += V^T P^T for the current
-// tile interleaved with S^T = K Q^T for the next tile (independent chains,
-// so neither waits on the other's results).
-template <int D, int NVMEM = 0>
+// tile (second half of the keys, then first half) around S^T = K Q^T for
+// the next tile (NKB independent chains that alternate, so that none waits
+// on its own previous result). The score tile is complete well before the
+// phase ends, so the next VALU phase can start on it at once. With DO_S
+// false only the value product is issued (last tile).
+template <int D, int BN, int NVMEM = 0, bool DO_S = true, bool DO_PV = true>
 __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const bf16x8* qf,
-                                           const u32x4* pw, const VtOffsets& vo, int lq, int h,
-                                           f32x16* sacc, f32x16* oacc) {
-  using T = FwdTile<D>;
-  constexpr int SPT = T::DK / 4;  // score k-steps per 16-key step of the value product
+                                           const u32x4* pw, const VtOffsets<BN>& vo, int lq, int h,
+                                           const bf16x8* pre, f32x16* sacc, f32x16* oacc) {
+  using T = FwdTile<D, BN>;
   const bf16* k0 = kt + lq * T::KPITCH + 8 * h;
-  const bf16* k1 = k0 + 32 * T::KPITCH;
-  f32x16 a0, a1;
+  constexpr int NPV = DO_PV ? T::NT * T::DB : 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a0[i] = a1[i] = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const bf16x8 pf = as_bf16x8(pw[t]);
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) oacc[db] = mfma32x32x16(vt_read<D>(vt, vo, t, db), pf, oacc[db]);
-#pragma unroll
-    for (int s = SPT * t; s < SPT * (t + 1); ++s) {
-      a0 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 16 * s)), qf[s], a0);
-      a1 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k1 + 16 * s)), qf[s], a1);
-    }
+  for (int k = 0; k < NPV / 2; ++k) {
+    const int t = pv_step_t<T::NT>(k, T::DB), db = k % T::DB;
+    const bf16x8 vf = k < kPrefetch ? pre[k] : vt_read<BN>(vt, vo, t, db);
+    oacc[db] = mfma32x32x16(vf, as_bf16x8(pw[t]), oacc[db]);
   }
-  interleave_lds_mfma<4 * T::DB + 2 * T::DK, 3, NVMEM>();
-  sacc[0] = a0;
-  sacc[1] = a1;
+  if (DO_S) {
+    f32x16 a[T::NKB];
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a[kb][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < T::DK; ++s)
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+        a[kb] = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 32 * kb * T::KPITCH + 16 * s)), qf[s], a[kb]);
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb) sacc[kb] = a[kb];
+  }
+#pragma unroll
+  for (int k = NPV / 2; k < NPV; ++k) {
+    const int t = pv_step_t<T::NT>(k, T::DB), db = k % T::DB;
+    oacc[db] = mfma32x32x16(vt_read<BN>(vt, vo, t, db), as_bf16x8(pw[t]), oacc[db]);
+  }
+  // Issue order: global loads, then one LDS read after each MFMA, which
+  // keeps kPrefetch operands in flight (without the prefetched value
+  // operands, the first kPrefetch reads go ahead of the first MFMA).
+  constexpr int NMFMA = NPV + (DO_S ? T::NKB * T::DK : 0);
+  if (NVMEM > 0) __builtin_amdgcn_sched_group_barrier(0x020, NVMEM, 0);
+  if (!DO_PV) __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + kPrefetch < NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
 }
 
 // Epilogue: O = o / l (bf16), LSE = ln 2 (m + log2 l).
@@ -294,9 +346,9 @@ __device__ __forceinline__ void transpose_v_pair(u32x4 a, u32x4 b, u32x4& lo, u3
 // threads: global -> registers (buffer loads: rows >= N read as zeros),
 // then registers -> LDS. K chunks are spread over all threads; V is staged
 // in passes of VKEYS keys per wave (each lane: two 16-byte loads).
-template <int D, int ROWS, int THREADS>
+template <int D, int ROWS, int THREADS, int BN = 64>
 struct Stager {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, BN>;
   static constexpr int WAVES = THREADS / 64;
   static constexpr int KCPT = ROWS * T::CPR / THREADS;  // K chunks per thread
   static constexpr int VPASS = ROWS / T::VKEYS;          // V passes in total
@@ -341,8 +393,8 @@ struct Stager {
         u32x4 lo, hi;
         transpose_v_pair(va[i], vb[i], lo, hi);
         const int slot = (r0 + pass * T::VKEYS) / 8 + g;
-        *(u32x4*)(vt + d0 * T::BN + 8 * (slot ^ vt_swz(d0))) = lo;
-        *(u32x4*)(vt + (d0 + 1) * T::BN + 8 * (slot ^ vt_swz(d0 + 1))) = hi;
+        *(u32x4*)(vt + d0 * BN + 8 * (slot ^ vt_swz<BN>(d0))) = lo;
+        *(u32x4*)(vt + (d0 + 1) * BN + 8 * (slot ^ vt_swz<BN>(d0 + 1))) = hi;
       }
     }
   }
@@ -378,7 +430,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
-  const VtOffsets vo(lq, h);
+  const VtOffsets<64> vo(lq, h);
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
@@ -438,14 +490,22 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 // in time but one tile ahead: K_{j+3}, V_{j+2}), which keeps each buffer
 // free until both groups have read it.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                    const bf16* __restrict__ V, bf16* __restrict__ O,
                                    float* __restrict__ LSE, int N, int n_qtiles, int total_tiles,
                                    float c, int remap) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, BN>;
   constexpr int BM = 256;
+  // With 64-key tiles each group issues the global loads of its staging
+  // share at the start of its MFMA phase (a phase before writing them to
+  // LDS); with 128-key tiles the staging registers would not fit beside the
+  // larger score tile there, so the loads go out at the start of the VALU
+  // phase and are written after the softmax.
+  constexpr bool kEarlyLoads = BN == 64;
+  using StG = Stager<D, BN / 2, 256, BN>;
+  constexpr int NVMEM = StG::KCPT + (StG::VPASS % StG::WAVES == 0 ? 2 * StG::VPW : 0);
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::STAGE];
   auto ks = [&](int b) { return smem + (b & 1) * T::STAGE; };
   auto vs = [&](int b) { return smem + (b & 1) * T::STAGE + T::KTILE; };
@@ -459,10 +519,10 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int grp = wave >> 2;          // 0: group A, 1: group B
   const int gtid = tid & 255;         // thread index within the group
-  const int r0 = 32 * grp;            // rows of each tile this group stages
+  const int r0 = (BN / 2) * grp;      // rows of each tile this group stages
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
-  const VtOffsets vo(lq, h);
+  const VtOffsets<BN> vo(lq, h);
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
@@ -477,7 +537,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   const bool ragged_tail = (N % T::BN) != 0;
 
   {  // prologue: everyone stages K_0, V_0 and K_1
-    Stager<D, 64, 512> st0;
+    Stager<D, BN, 512, BN> st0;
     st0.load(krs, vrs, 0, 0, 0, tid);
     st0.store(ks(0), vs(0), 0, tid);
     st0.load(krs, vrs, 1, 1, 0, tid);
@@ -486,36 +546,44 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   __syncthreads();
   if (grp == 1) phase_barrier();
 
-  f32x16 sacc[2];
-  u32x4 pw[4];
+  f32x16 sacc[T::NKB];
+  u32x4 pw[T::NT];
+  bf16x8 pre[kPrefetch];  // first V^T operands of the next MFMA phase
   // Group A stages (K_{j+2}, V_{j+1}) in VALU phase j, group B (K_{j+3}, V_{j+2}).
   // Tiles past the end are zero-filled without memory traffic into buffers
   // no wave reads any more.
-  Stager<D, 32, 256> st;
+  StG st;
 
-  score_tile<D>(ks(0), qf, lq, h, sacc);  // MFMA phase of tile 0
+  // MFMA phase of tile 0: scores only
+  mfma_phase<D, BN, 0, true, false>(ks(0), vs(0), qf, pw, vo, lq, h, pre, sacc, oacc);
   phase_barrier();
   if (grp == 1) st.load(krs, vrs, 2, 1, r0, gtid);  // VALU phase "j = -1"
   if (n_kt == 1 && ragged_tail)
-    softmax_tile<true, T::DB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
+    softmax_tile<true, T::DB, T::NKB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
   else
-    softmax_tile<false, T::DB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
+    softmax_tile<false, T::DB, T::NKB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
   if (grp == 1) st.store(ks(2), vs(1), r0, gtid);
+  prefetch_pv<D, BN>(vs(0), vo, pre);
   phase_barrier();
 
   auto body = [&](auto ragged, int j) {
-    // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1. The global
-    // loads of this group's share of later tiles are issued here, a phase
-    // before they are written to LDS, so their latency is hidden.
+    constexpr bool RAGGED = decltype(ragged)::value;
+    // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1.
     const int tk = j + 2 + grp, tv = j + 1 + grp;
-    st.load(krs, vrs, tk, tv, r0, gtid);
-    mfma_phase<D, Stager<D, 32, 256>::KCPT + (Stager<D, 32, 256>::VPASS % 4 == 0 ? 2 : 0)>(
-        ks(j + 1), vs(j), qf, pw, vo, lq, h, sacc, oacc);
+    if (kEarlyLoads) st.load(krs, vrs, tk, tv, r0, gtid);
+    mfma_phase<D, BN, kEarlyLoads ? NVMEM : 0>(ks(j + 1), vs(j), qf, pw, vo, lq, h, pre, sacc,
+                                               oacc);
     phase_barrier();
-    // VALU phase: online softmax of tile j+1, staging of later tiles.
-    softmax_tile<decltype(ragged)::value, T::DB>(sacc, c, (j + 1) * T::BN, N, h, m_run, l_run,
-                                                 oacc, pw);
-    st.store(ks(tk), vs(tv), r0, gtid);
+    // VALU phase: staging of later tiles (with early loads first, so that
+    // the LDS writes drain under the softmax), online softmax of tile j+1,
+    // and the first operand reads of the next MFMA phase.
+    if (kEarlyLoads)
+      st.store(ks(tk), vs(tv), r0, gtid);
+    else
+      st.load(krs, vrs, tk, tv, r0, gtid);
+    softmax_tile<RAGGED, T::DB, T::NKB>(sacc, c, (j + 1) * T::BN, N, h, m_run, l_run, oacc, pw);
+    if (!kEarlyLoads) st.store(ks(tk), vs(tv), r0, gtid);
+    prefetch_pv<D, BN>(vs(j + 1), vo, pre);
     phase_barrier();
   };
   // bodies j = 0 .. n_kt - 2; only the one that takes the softmax of a
@@ -529,7 +597,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
     ++j;
   }
   // last tile: value product only
-  pv_tile<D>(vs(j), pw, vo, oacc);
+  mfma_phase<D, BN, 0, false>(ks(j), vs(j), qf, pw, vo, lq, h, pre, sacc, oacc);
   phase_barrier();
   phase_barrier();
   if (grp == 0) phase_barrier();
@@ -651,6 +719,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Keys per ping-pong phase: 128 halves the number of phases (and so the
+// per-phase cost of barriers and of refilling the operand pipeline).
+constexpr int kPingPongBN = 128;
+
 template <int D, int NW>
 static hipError_t launch_bf16(const FwdArgs& a) {
   constexpr int BM = 32 * NW;
@@ -659,7 +731,7 @@ static hipError_t launch_bf16(const FwdArgs& a) {
   if (total > INT32_MAX) return hipErrorInvalidValue;
   const int remap = (total % 8 == 0) ? 1 : 0;
   if constexpr (NW == 8) {
-    hipLaunchKernelGGL((attn_fwd_bf16_pingpong_kernel<D>), dim3((unsigned)total), dim3(512), 0,
+    hipLaunchKernelGGL((attn_fwd_bf16_pingpong_kernel<D, kPingPongBN>), dim3((unsigned)total), dim3(512), 0,
                        (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (bf16*)a.o, a.lse, (int)a.N, n_qtiles, (int)total,
                        a.scale * kLog2e, remap);
