@@ -56,20 +56,14 @@ struct FwdTile {
   static constexpr int VKEYS = 128 / CPR;    // keys one wave transposes per pass
 };
 
-// XOR swizzle of the 16-byte slots of V^T row d (BN / 8 slots per row).
-// Reads of one MFMA operand touch 16 consecutive rows at one logical slot;
-// the transposed writes touch rows d = 8r + e (r = 0..15) at one slot.
-//   BN = 64 (128-byte rows, two per bank period): (d & 1, vt_swz(d)) is
-//     distinct over 16 consecutive rows (no read conflict); vt_swz takes
-//     each value twice over the written rows (two-way write conflict).
-//   BN = 128 (256-byte rows): vt_swz is a bijection over 16 consecutive
-//     rows and over the written rows (no conflict either way).
-// In both, vt_swz(32 b + x) = vt_swz(x) ^ 2 b for x < 32, b < 4.
-template <int BN>
-__device__ __forceinline__ int vt_swz(int d) {
-  if constexpr (BN == 64) return ((d >> 1) ^ (d >> 4)) & 7;
-  else return (d ^ (d >> 4)) & 15;
-}
+// A V^T tile of BN keys is BN / 64 sub-tiles of D rows x 64 keys (128-byte
+// rows). vt_swz is the XOR swizzle of the 8 sixteen-byte slots of row d:
+// reads of one MFMA operand touch 16 consecutive rows at one logical slot,
+// and (d & 1, vt_swz(d)) is distinct across them (no read conflict); the
+// transposed writes touch rows d = 8r + e (r = 0..15) at one slot, where
+// vt_swz takes each value twice (two-way write conflict). Also
+// vt_swz(32 b + x) = vt_swz(x) ^ 2 b for x < 32, b < 4.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
 
 // Buffer resource over one head's [N, D] K or V slice. A load whose byte
 // offset is at or past N * D * 2 returns zeros without touching memory,
@@ -91,23 +85,23 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
 constexpr float kLazyRescale = 8.0f;
 
 // Per-lane element offsets of the V^T operand reads: the A operand of step t,
-// d block db (rows d = 32 db + lq, keys 16 t + 8 h .. + 7) starts at
-// o[t ^ db] + db * 32 * BN. With d = 32 db + lq, vt_swz(d) = f0 ^ 2 db for
-// f0 = vt_swz(lq), so the swizzled slot (2 t + h) ^ vt_swz(d) equals
-// (2 (t ^ db) + h) ^ f0: BN / 16 per-lane offsets serve every read.
-template <int BN>
+// d block db (rows d = 32 db + lq, keys 16 t + 8 h .. + 7) sits in sub-tile
+// t / 4 at o[(t % 4) ^ db] + db * 32 * 64. With d = 32 db + lq,
+// vt_swz(d) = f0 ^ 2 db for f0 = vt_swz(lq), so the swizzled slot
+// (2 (t % 4) + h) ^ vt_swz(d) equals (2 ((t % 4) ^ db) + h) ^ f0: four
+// per-lane offsets serve every read.
 struct VtOffsets {
-  int o[BN / 16];
+  int o[4];
   __device__ __forceinline__ VtOffsets(int lq, int h) {
-    const int f0 = vt_swz<BN>(lq);
+    const int f0 = vt_swz(lq);
 #pragma unroll
-    for (int u = 0; u < BN / 16; ++u) o[u] = lq * BN + 8 * ((2 * u + h) ^ f0);
+    for (int u = 0; u < 4; ++u) o[u] = lq * 64 + 8 * ((2 * u + h) ^ f0);
   }
 };
 
-template <int BN>
-__device__ __forceinline__ bf16x8 vt_read(const bf16* vt, const VtOffsets<BN>& vo, int t, int db) {
-  return as_bf16x8(*(const u32x4*)(vt + vo.o[t ^ db] + db * 32 * BN));
+template <int D>
+__device__ __forceinline__ bf16x8 vt_read(const bf16* vt, const VtOffsets& vo, int t, int db) {
+  return as_bf16x8(*(const u32x4*)(vt + (t >> 2) * D * 64 + vo.o[(t & 3) ^ db] + db * 32 * 64));
 }
 
 // Issue order of a run of NMFMA MFMAs that each consume one LDS read: the
@@ -202,14 +196,14 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
 
 // O^T += V^T P^T for one 64-key tile: step t covers keys 16 t + 8 h + 0..7.
 template <int D>
-__device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, const VtOffsets<64>& vo,
+__device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, const VtOffsets& vo,
                                         f32x16* oacc) {
   using T = FwdTile<D>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const bf16x8 pf = as_bf16x8(pw[t]);
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) oacc[db] = mfma32x32x16(vt_read<64>(vt, vo, t, db), pf, oacc[db]);
+    for (int db = 0; db < T::DB; ++db) oacc[db] = mfma32x32x16(vt_read<D>(vt, vo, t, db), pf, oacc[db]);
   }
   interleave_lds_mfma<4 * T::DB>();
 }
@@ -227,10 +221,10 @@ constexpr int kPrefetch = 3;  // V^T operand reads issued before the barrier
 
 // First kPrefetch V^T operands of the next MFMA phase (see pv_step_t).
 template <int D, int BN>
-__device__ __forceinline__ void prefetch_pv(const bf16* vt, const VtOffsets<BN>& vo, bf16x8* pre) {
+__device__ __forceinline__ void prefetch_pv(const bf16* vt, const VtOffsets& vo, bf16x8* pre) {
   using T = FwdTile<D, BN>;
 #pragma unroll
-  for (int k = 0; k < kPrefetch; ++k) pre[k] = vt_read<BN>(vt, vo, pv_step_t<T::NT>(k, T::DB), k % T::DB);
+  for (int k = 0; k < kPrefetch; ++k) pre[k] = vt_read<D>(vt, vo, pv_step_t<T::NT>(k, T::DB), k % T::DB);
 }
 
 // One MFMA phase of the ping-pong schedule: O^T += V^T P^T for the current
@@ -241,7 +235,7 @@ __device__ __forceinline__ void prefetch_pv(const bf16* vt, const VtOffsets<BN>&
 // false only the value product is issued (last tile).
 template <int D, int BN, int NVMEM = 0, bool DO_S = true, bool DO_PV = true>
 __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const bf16x8* qf,
-                                           const u32x4* pw, const VtOffsets<BN>& vo, int lq, int h,
+                                           const u32x4* pw, const VtOffsets& vo, int lq, int h,
                                            const bf16x8* pre, f32x16* sacc, f32x16* oacc) {
   using T = FwdTile<D, BN>;
   const bf16* k0 = kt + lq * T::KPITCH + 8 * h;
@@ -249,7 +243,7 @@ __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const
 #pragma unroll
   for (int k = 0; k < NPV / 2; ++k) {
     const int t = pv_step_t<T::NT>(k, T::DB), db = k % T::DB;
-    const bf16x8 vf = k < kPrefetch ? pre[k] : vt_read<BN>(vt, vo, t, db);
+    const bf16x8 vf = k < kPrefetch ? pre[k] : vt_read<D>(vt, vo, t, db);
     oacc[db] = mfma32x32x16(vf, as_bf16x8(pw[t]), oacc[db]);
   }
   if (DO_S) {
@@ -269,7 +263,7 @@ __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const
 #pragma unroll
   for (int k = NPV / 2; k < NPV; ++k) {
     const int t = pv_step_t<T::NT>(k, T::DB), db = k % T::DB;
-    oacc[db] = mfma32x32x16(vt_read<BN>(vt, vo, t, db), as_bf16x8(pw[t]), oacc[db]);
+    oacc[db] = mfma32x32x16(vt_read<D>(vt, vo, t, db), as_bf16x8(pw[t]), oacc[db]);
   }
   // Issue order: global loads, then one LDS read after each MFMA, which
   // keeps kPrefetch operands in flight (without the prefetched value
@@ -393,8 +387,9 @@ struct Stager {
         u32x4 lo, hi;
         transpose_v_pair(va[i], vb[i], lo, hi);
         const int slot = (r0 + pass * T::VKEYS) / 8 + g;
-        *(u32x4*)(vt + d0 * BN + 8 * (slot ^ vt_swz<BN>(d0))) = lo;
-        *(u32x4*)(vt + (d0 + 1) * BN + 8 * (slot ^ vt_swz<BN>(d0 + 1))) = hi;
+        bf16* sub = vt + (slot >> 3) * D * 64;  // 64-key sub-tile
+        *(u32x4*)(sub + d0 * 64 + 8 * ((slot & 7) ^ vt_swz(d0))) = lo;
+        *(u32x4*)(sub + (d0 + 1) * 64 + 8 * ((slot & 7) ^ vt_swz(d0 + 1))) = hi;
       }
     }
   }
@@ -430,7 +425,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
-  const VtOffsets<64> vo(lq, h);
+  const VtOffsets vo(lq, h);
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
@@ -522,7 +517,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   const int r0 = (BN / 2) * grp;      // rows of each tile this group stages
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
-  const VtOffsets<BN> vo(lq, h);
+  const VtOffsets vo(lq, h);
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
