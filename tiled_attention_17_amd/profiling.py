@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FWD_KERNEL = "attn_fwd_bf16_kernel"
+FWD_KERNEL = "attn_fwd_bf16_pingpong_kernel"
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_17_amd", "csrc", f)
                   for f in ("attn_fwd.hip", "device_common.h")]
 
@@ -129,7 +129,15 @@ def summarize(fetch_dir, write_dir, stats_dir, copy_mib, out_json, out_txt):
         json.dump(res, f, indent=2)
     lines = [f"# HBM traffic of {FWD_KERNEL} on {w.name}", "",
              "Counters FETCH_SIZE and WRITE_SIZE (one rocprofv3 --pmc run each), scaled by the",
-             f"same counters on a {copy_mib} MiB device-to-device copy.", ""]
+             f"same counters on a {copy_mib} MiB device-to-device copy. Commands (repo root):", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv \\",
+             "        -- python3 tiled_attention_17_amd/profiling.py run",
+             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv \\",
+             "        -- python3 tiled_attention_17_amd/profiling.py run",
+             "    python3 -m tiled_attention_17_amd.profiling summarize --fetch gpurun_out/pmc_fetch \\",
+             "        --write gpurun_out/pmc_write", "",
+             f"The copy reads {copy_bytes} bytes and writes as many; the counters read "
+             f"{max(fc):.0f} and {max(wc):.0f} units for it, which gives the scale factors below.", ""]
     for k, v in res.items():
         lines.append(f"- {k}: {v}")
     if stats_dir:
