@@ -46,8 +46,7 @@ struct FwdTile {
   static constexpr int BN = BN_;             // keys per step (64 or 128)
   static constexpr int NKB = BN / 32;        // 32-key blocks of a score tile
   static constexpr int NT = BN / 16;         // 16-key steps of the value product
-  static constexpr int KPITCH = D + 8;       // K row pitch (bf16): row stride = 4 banks mod 64
-  static constexpr int KTILE = BN * KPITCH;  // K tile, bf16 elements
+  static constexpr int KTILE = BN * D;       // K tile, bf16 elements (rows of D, chunk-swizzled)
   static constexpr int VTILE = D * BN;       // V^T tile: D rows of BN keys, no padding
   static constexpr int STAGE = KTILE + VTILE;
   static constexpr int DK = D / 16;          // k-steps of the score product
@@ -55,6 +54,42 @@ struct FwdTile {
   static constexpr int CPR = D / 8;          // 16-byte chunks per K or V row
   static constexpr int VKEYS = 128 / CPR;    // keys one wave transposes per pass
 };
+
+// K tiles hold key swap23(r) at LDS row r (rows of D bf16, no padding); the
+// 16-byte chunk c of row r sits at chunk position c ^ kswz(r). An operand
+// read touches 16 consecutive rows at one logical chunk: for D = 128
+// (256-byte rows) kswz(r) = r & 15 spreads them over the 16 chunk positions
+// of a bank period, for D = 64 (128-byte rows, two per period)
+// (r & 1, kswz(r)) = (r & 1, (r >> 1) & 7) does. kswz(32 b + r) = kswz(r).
+// The layout is written lane-linearly by buffer_load ... lds (1 KB per
+// instruction), so no padding is possible and the swizzle is what keeps the
+// reads free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+
+// Per-lane element offsets of the K operand reads: step s of key block kb
+// (row 32 kb + lq, logical chunk 2 s + h) is at o(s) + 32 kb D, where
+// o(s) = lq D + 8 ((2 s + h) ^ kswz(lq)) = (lq D + 8 (h ^ kswz(lq))) ^ 16 s
+// (the chunk bits sit below the row bits). COMPACT keeps one register and
+// does the XOR per read; otherwise all D / 16 offsets are kept.
+template <int D, bool COMPACT = false>
+struct KOffsets {
+  int o[COMPACT ? 1 : D / 16];
+  __device__ __forceinline__ KOffsets(int lq, int h) {
+    if (COMPACT) {
+      o[0] = lq * D + 8 * (h ^ kswz<D>(lq));
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) o[s] = lq * D + 8 * ((2 * s + h) ^ kswz<D>(lq));
+    }
+  }
+  __device__ __forceinline__ int at(int s) const { return COMPACT ? (o[0] ^ (16 * s)) : o[s]; }
+};
+
+template <int D, bool COMPACT>
+__device__ __forceinline__ bf16x8 k_read(const bf16* kt, const KOffsets<D, COMPACT>& ko, int s, int kb) {
+  return as_bf16x8(*(const u32x4*)(kt + ko.at(s) + 32 * kb * D));
+}
 
 // A V^T tile of BN keys is BN / 64 sub-tiles of D rows x 64 keys (128-byte
 // rows). vt_swz is the XOR swizzle of the 8 sixteen-byte slots of row d:
@@ -125,18 +160,16 @@ __device__ __forceinline__ void interleave_lds_mfma() {
 // S^T = K Q^T for one 64-key tile whose rows sit at swap23(key) in `kt`.
 // sacc[kb][i] then holds key 32 kb + 16 (i/8) + 8 h + i%8 for this lane's query.
 template <int D>
-__device__ __forceinline__ void score_tile(const bf16* kt, const bf16x8* qf, int lq, int h,
-                                           f32x16* sacc) {
+__device__ __forceinline__ void score_tile(const bf16* kt, const bf16x8* qf,
+                                           const KOffsets<D, true>& ko, f32x16* sacc) {
   using T = FwdTile<D>;
   f32x16 a0, a1;
 #pragma unroll
   for (int i = 0; i < 16; ++i) a0[i] = a1[i] = 0.f;
-  const bf16* k0 = kt + lq * T::KPITCH + 8 * h;
-  const bf16* k1 = k0 + 32 * T::KPITCH;
 #pragma unroll
   for (int s = 0; s < T::DK; ++s) {
-    a0 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 16 * s)), qf[s], a0);
-    a1 = mfma32x32x16(as_bf16x8(*(const u32x4*)(k1 + 16 * s)), qf[s], a1);
+    a0 = mfma32x32x16(k_read<D>(kt, ko, s, 0), qf[s], a0);
+    a1 = mfma32x32x16(k_read<D>(kt, ko, s, 1), qf[s], a1);
   }
   interleave_lds_mfma<2 * T::DK>();
   sacc[0] = a0;
@@ -235,10 +268,10 @@ __device__ __forceinline__ void prefetch_pv(const bf16* vt, const VtOffsets& vo,
 // false only the value product is issued (last tile).
 template <int D, int BN, int NVMEM = 0, bool DO_S = true, bool DO_PV = true>
 __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const bf16x8* qf,
-                                           const u32x4* pw, const VtOffsets& vo, int lq, int h,
-                                           const bf16x8* pre, f32x16* sacc, f32x16* oacc) {
+                                           const u32x4* pw, const VtOffsets& vo,
+                                           const KOffsets<D>& ko, const bf16x8* pre, f32x16* sacc,
+                                           f32x16* oacc) {
   using T = FwdTile<D, BN>;
-  const bf16* k0 = kt + lq * T::KPITCH + 8 * h;
   constexpr int NPV = DO_PV ? T::NT * T::DB : 0;
 #pragma unroll
   for (int k = 0; k < NPV / 2; ++k) {
@@ -256,7 +289,7 @@ __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const
     for (int s = 0; s < T::DK; ++s)
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
-        a[kb] = mfma32x32x16(as_bf16x8(*(const u32x4*)(k0 + 32 * kb * T::KPITCH + 16 * s)), qf[s], a[kb]);
+        a[kb] = mfma32x32x16(k_read<D>(kt, ko, s, kb), qf[s], a[kb]);
 #pragma unroll
     for (int kb = 0; kb < T::NKB; ++kb) sacc[kb] = a[kb];
   }
@@ -340,16 +373,16 @@ __device__ __forceinline__ void transpose_v_pair(u32x4 a, u32x4 b, u32x4& lo, u3
 // threads: global -> registers (buffer loads: rows >= N read as zeros),
 // then registers -> LDS. K chunks are spread over all threads; V is staged
 // in passes of VKEYS keys per wave (each lane: two 16-byte loads).
-template <int D, int ROWS, int THREADS, int BN = 64>
+template <int D, int ROWS, int THREADS, int BN = 64, bool WITH_K = true>
 struct Stager {
   using T = FwdTile<D, BN>;
   static constexpr int WAVES = THREADS / 64;
-  static constexpr int KCPT = ROWS * T::CPR / THREADS;  // K chunks per thread
+  static constexpr int KCPT = WITH_K ? ROWS * T::CPR / THREADS : 0;  // K chunks per thread
   static constexpr int VPASS = ROWS / T::VKEYS;          // V passes in total
   static constexpr int VPW = (VPASS + WAVES - 1) / WAVES;
-  static_assert(ROWS * T::CPR % THREADS == 0, "K rows must split evenly over the threads");
+  static_assert(!WITH_K || ROWS * T::CPR % THREADS == 0, "K rows must split evenly over the threads");
   static_assert(ROWS % T::VKEYS == 0, "V rows must split into whole passes");
-  u32x4 k[KCPT], va[VPW], vb[VPW];
+  u32x4 k[KCPT > 0 ? KCPT : 1], va[VPW], vb[VPW];
 
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                        int kt_k, int kt_v, int r0, int t) {
@@ -376,7 +409,8 @@ struct Stager {
     for (int i = 0; i < KCPT; ++i) {
       const int ch = t + i * THREADS;
       const int row = r0 + ch / T::CPR, col = (ch % T::CPR) * 8;
-      *(u32x4*)(kt + swap23(row) * T::KPITCH + col) = k[i];
+      const int lr = swap23(row);
+      *(u32x4*)(kt + lr * D + 8 * ((col / 8) ^ kswz<D>(lr))) = k[i];
     }
     const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
     const int d0 = 8 * (r % T::CPR) + 2 * p, g = r / T::CPR;
@@ -394,6 +428,51 @@ struct Stager {
     }
   }
 };
+
+// Rows [r0, r0 + ROWS) of a K tile staged straight into LDS by WAVES waves
+// with buffer_load ... lds: each instruction writes 1 KB of LDS
+// lane-linearly (lane L -> 16 bytes at L * 16), and each lane loads the
+// global chunk that belongs there in the swizzled layout (LDS row r holds
+// key swap23(r), chunk position p holds logical chunk p ^ kswz(r)). The
+// per-lane byte offsets within a tile are fixed, the tile's base goes in the
+// scalar offset, so staging a tile costs no VALU work. Rows >= N read as
+// zeros (buffer range check). Completion is waited for with vmcnt before
+// the barrier that publishes the tile.
+// One buffer_load_dwordx4 ... lds: 16 bytes per lane from byte offset
+// voff + soff of the buffer to LDS address lds + 16 * lane. (A plain device
+// function: the host pass of a kernel template must not see the builtin.)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           soff, 0, 0);
+}
+
+template <int D, int ROWS, int WAVES = 4>
+struct KDirect {
+  static constexpr int RPI = 1024 / (2 * D);              // rows per instruction
+  static constexpr int NI = ROWS / (WAVES * RPI);         // instructions per wave
+  static_assert(ROWS % (WAVES * RPI) == 0, "rows must split evenly over the waves");
+  int voff[NI];
+  int lds_row0;  // first LDS row of this wave's first instruction
+  __device__ __forceinline__ KDirect(int r0, int wave_in_group, int lane) {
+    lds_row0 = r0 + wave_in_group * NI * RPI;
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int lr = lds_row0 + i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ kswz<D>(lr);
+      voff[i] = (swap23(lr) * D + 8 * c) * 2;
+    }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, int tile, int bn, bf16* kt) const {
+    const int soff = tile * bn * D * 2;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) lds_dma16(kr, kt + (lds_row0 + i * RPI) * D, voff[i], soff);
+  }
+};
+
+// Waits until this wave's vector-memory operations are done (among them the
+// buffer_load ... lds writes of a directly staged K tile).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -426,6 +505,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
   const VtOffsets vo(lq, h);
+  const KOffsets<D, true> ko(lq, h);
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
@@ -438,24 +518,30 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   float m_run = -INFINITY, l_run = 0.f;
 
   const int n_kt = (N + T::BN - 1) / T::BN;
-  // The next tile is staged in two halves of 32 rows (the first half's
-  // loads overlap the score product and softmax, the second half's the
-  // value product), which halves the staging registers.
-  Stager<D, 32, NW * 64> st;
+  // The next tile's K goes straight to LDS; its V is staged through
+  // registers in two halves of 32 rows (the first half's loads overlap the
+  // score product and softmax, the second half's the value product).
+  const KDirect<D, 64, NW> kd(0, wave, lane);
+  Stager<D, 32, NW * 64, 64, false> st;
+  kd.load(krs, 0, 64, ks(0));
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     st.load(krs, vrs, 0, 0, 32 * half, tid);
     st.store(ks(0), vs(0), 32 * half, tid);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int j = 0; j < n_kt; ++j) {
     const int cur = j & 1;
     const bool more = j + 1 < n_kt;
-    if (more) st.load(krs, vrs, j + 1, j + 1, 0, tid);
+    if (more) {
+      kd.load(krs, j + 1, 64, ks(cur ^ 1));
+      st.load(krs, vrs, j + 1, j + 1, 0, tid);
+    }
     f32x16 sacc[2];
     u32x4 pw[4];
-    score_tile<D>(ks(cur), qf, lq, h, sacc);
+    score_tile<D>(ks(cur), qf, ko, sacc);
     if ((j + 1) * T::BN > N)
       softmax_tile<true, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
     else
@@ -466,6 +552,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     }
     pv_tile<D>(vs(cur), pw, vo, oacc);
     if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 32, tid);
+    wait_vmem();  // K tile written to LDS
     __syncthreads();
   }
   store_output<D>(oacc, m_run, l_run, O + base + (size_t)q_row * D, LSE + (size_t)bh * N + q_row,
@@ -499,7 +586,9 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   // larger score tile there, so the loads go out at the start of the VALU
   // phase and are written after the softmax.
   constexpr bool kEarlyLoads = BN == 64;
-  using StG = Stager<D, BN / 2, 256, BN>;
+  // K is staged straight into LDS at 128-key width, through registers at 64
+  constexpr bool kDirectK = BN == 128;
+  using StG = Stager<D, BN / 2, 256, BN, !kDirectK>;
   constexpr int NVMEM = StG::KCPT + (StG::VPASS % StG::WAVES == 0 ? 2 * StG::VPW : 0);
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::STAGE];
   auto ks = [&](int b) { return smem + (b & 1) * T::STAGE; };
@@ -518,6 +607,11 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   const int q_row = qt * BM + wave * 32 + lq;
   const bool q_ok = q_row < N;
   const VtOffsets vo(lq, h);
+  const KOffsets<D> ko(lq, h);
+  const KDirect<D, BN / 2> kd(r0, wave & 3, lane);
+  auto stage_k = [&](int t) {  // this group's rows of K tile t (direct mode)
+    if (kDirectK) kd.load(krs, t, BN, ks(t));
+  };
 
   bf16x8 qf[T::DK];
   load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
@@ -550,15 +644,19 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   StG st;
 
   // MFMA phase of tile 0: scores only
-  mfma_phase<D, BN, 0, true, false>(ks(0), vs(0), qf, pw, vo, lq, h, pre, sacc, oacc);
+  mfma_phase<D, BN, 0, true, false>(ks(0), vs(0), qf, pw, vo, ko, pre, sacc, oacc);
   phase_barrier();
-  if (grp == 1) st.load(krs, vrs, 2, 1, r0, gtid);  // VALU phase "j = -1"
+  if (grp == 1) {  // VALU phase "j = -1"
+    stage_k(2);
+    st.load(krs, vrs, 2, 1, r0, gtid);
+  }
   if (n_kt == 1 && ragged_tail)
     softmax_tile<true, T::DB, T::NKB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
   else
     softmax_tile<false, T::DB, T::NKB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
   if (grp == 1) st.store(ks(2), vs(1), r0, gtid);
   prefetch_pv<D, BN>(vs(0), vo, pre);
+  if (kDirectK) wait_vmem();
   phase_barrier();
 
   auto body = [&](auto ragged, int j) {
@@ -566,19 +664,21 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
     // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1.
     const int tk = j + 2 + grp, tv = j + 1 + grp;
     if (kEarlyLoads) st.load(krs, vrs, tk, tv, r0, gtid);
-    mfma_phase<D, BN, kEarlyLoads ? NVMEM : 0>(ks(j + 1), vs(j), qf, pw, vo, lq, h, pre, sacc,
-                                               oacc);
+    mfma_phase<D, BN, kEarlyLoads ? NVMEM : 0>(ks(j + 1), vs(j), qf, pw, vo, ko, pre, sacc, oacc);
     phase_barrier();
     // VALU phase: staging of later tiles (with early loads first, so that
     // the LDS writes drain under the softmax), online softmax of tile j+1,
     // and the first operand reads of the next MFMA phase.
-    if (kEarlyLoads)
+    if (kEarlyLoads) {
       st.store(ks(tk), vs(tv), r0, gtid);
-    else
+    } else {
+      stage_k(tk);
       st.load(krs, vrs, tk, tv, r0, gtid);
+    }
     softmax_tile<RAGGED, T::DB, T::NKB>(sacc, c, (j + 1) * T::BN, N, h, m_run, l_run, oacc, pw);
     if (!kEarlyLoads) st.store(ks(tk), vs(tv), r0, gtid);
     prefetch_pv<D, BN>(vs(j + 1), vo, pre);
+    if (kDirectK) wait_vmem();  // K tile written to LDS
     phase_barrier();
   };
   // bodies j = 0 .. n_kt - 2; only the one that takes the softmax of a
@@ -592,7 +692,7 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
     ++j;
   }
   // last tile: value product only
-  mfma_phase<D, BN, 0, false>(ks(j), vs(j), qf, pw, vo, lq, h, pre, sacc, oacc);
+  mfma_phase<D, BN, 0, false>(ks(j), vs(j), qf, pw, vo, ko, pre, sacc, oacc);
   phase_barrier();
   phase_barrier();
   if (grp == 0) phase_barrier();
