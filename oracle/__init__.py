@@ -8,12 +8,15 @@ and the oracle never imports the product library (they share no code).
 Sources (cited by page title and section; no line numbers):
   [L17]  "第17讲 Tensor Core、HBM、SRAM 与 FlashAttention" (zwxr.cn news 250415),
          §8.1 (scaled dot-product attention), §8.3 (online softmax state
-         m, l, o and its update rule), §8.4 (exact, not bitwise identical).
+         m, l, o and its update rule; masks and causal attention named as
+         part of a real kernel), §8.4 (exact, not bitwise identical),
+         §9.2 (prefill and decode).
   [N5]   "GPU 架构与大模型高效计算" -- CS336 Lecture 5 notes (kyc001.github.io),
          §7.1-§7.2 (tiling, online softmax, recomputation in the backward pass).
   [R5]   "CS336 Lecture 5 · GPUs, TPUs -- 中文 Lecture Note" (romanrose.github.io),
          section "FlashAttention 解析" (running max/sum correction) and the
-         English transcript at [01:14:15]-[01:16:33].
+         English transcript at [01:14:15]-[01:16:33] (softmax of a tile,
+         partial results written back to global memory, then continued).
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, invariants, library special cases, brute force and finite
@@ -26,4 +29,6 @@ from .attention import (  # noqa: F401
     online_softmax_forward,
     brute_force_forward,
     brute_force_backward,
+    causal_visible,
+    merge_partials,
 )
