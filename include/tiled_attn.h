@@ -15,7 +15,16 @@
  *
  * Layout. Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] arrays
  * (d innermost, no strides); LSE is a dense [B, H, N] float array. Every
- * pointer is a device pointer. Q, K and V share N (self-attention shape).
+ * pointer is a device pointer. attn_fwd and attn_bwd take Q, K and V of one
+ * length N; attn_fwd_ex takes N_q queries against N_k keys (Q, O: [B,H,N_q,d];
+ * K, V: [B,H,N_k,d]; LSE: [B,H,N_q]).
+ *
+ * Causal mask (attn_fwd_ex with ATTN_MASK_CAUSAL). The Lecture 17 page names
+ * masks and causal attention (end of §8.3) as part of a real attention
+ * kernel without defining them; here query i sees key j iff
+ * j <= i + (N_k - N_q), i.e. the N_q queries are the last N_q positions of the
+ * key sequence (for N_q = N_k: j <= i). A query that sees no key (only when
+ * N_q > N_k) gets O = 0 and LSE = -inf.
  *
  * Supported: d in {64, 128}; 1 <= N with N * d * 4 < 2^31 (one head is
  * addressed with 32-bit byte offsets; any N, a ragged last tile is masked);
@@ -61,6 +70,11 @@ typedef enum {
   ATTN_FP32 = 1  /* float storage and arithmetic */
 } attn_dtype;
 
+typedef enum {
+  ATTN_MASK_NONE = 0,   /* every query sees every key */
+  ATTN_MASK_CAUSAL = 1  /* query i sees key j iff j <= i + N_k - N_q */
+} attn_mask;
+
 /* Library interface version (increments on any ABI change). */
 int attn_version(void);
 
@@ -86,6 +100,73 @@ const char* attn_last_error(void);
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                      attn_dtype dtype, void* stream);
+
+/* Bytes of device workspace attn_fwd_ex needs for `num_splits` key splits:
+ * 0 for num_splits <= 1, else num_splits * B*H*N_q * (d + 1) * 4 (the fp32
+ * partial O and LSE of every split). 0 also for invalid sizes. */
+size_t attn_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                   int64_t num_splits, attn_dtype dtype);
+
+/* Number of key splits attn_fwd_ex picks with num_splits = 0 on the current
+ * device: 1 when the query tiles alone give every compute unit work, else
+ * enough splits for about two workgroups per compute unit (each split at
+ * least 256 keys), at most 128. 0 on invalid sizes or a HIP error. */
+int64_t attn_fwd_ex_auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                attn_dtype dtype);
+
+/*
+ * Forward pass with N_q queries against N_k keys, an optional causal mask,
+ * and an optional split of the key range.
+ *   q         [B,H,Nq,d] input of type `dtype`, 16-byte aligned.
+ *   k, v      [B,H,Nk,d] inputs of type `dtype`, 16-byte aligned (may be
+ *             NULL when Nk = 0: then every row gets O = 0, LSE = -inf).
+ *   o, lse    [B,H,Nq,d] and [B,H,Nq] outputs as in attn_fwd.
+ *   mask      ATTN_MASK_NONE or ATTN_MASK_CAUSAL (see the header comment).
+ *   num_splits
+ *             1: one pass over all keys per query tile (workspace unused,
+ *             may be NULL); 2 .. 128: the keys are cut into that many ranges
+ *             of whole 128-key tiles (fewer when N_k is short), each range's
+ *             attention is computed by its own workgroups into `workspace`
+ *             as an fp32 (O_r, LSE_r) pair, and a second kernel merges them
+ *             (attn_merge's rule); 0: the library's choice
+ *             (attn_fwd_ex_auto_splits).
+ *   workspace device scratch of at least attn_fwd_ex_workspace_bytes() for
+ *             the split count used, 16-byte aligned, owned by the caller,
+ *             contents on entry ignored; must not overlap anything else.
+ * Source: Lecture 17 page §8.1-§8.3 (the computation), end of §8.3 (masks
+ * and causal attention), §9.2 (prefill and decode: few queries against a
+ * long key sequence); the split follows the partial results written back to
+ * global memory and continued from in the CS336 Lecture 5 transcript
+ * (FlashAttention passage). attn_fwd(q,k,v,o,lse,B,H,N,d,...) equals
+ * attn_fwd_ex with Nq = Nk = N, ATTN_MASK_NONE, num_splits = 1.
+ * Errors as for attn_fwd; also an unknown mask, num_splits outside 0 .. 128,
+ * or a missing or too small workspace (ATTN_ERR_INVALID_ARGUMENT).
+ */
+attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                        attn_mask mask, int64_t num_splits, void* workspace,
+                        size_t workspace_bytes, attn_dtype dtype, void* stream);
+
+/*
+ * Merge of attention results over disjoint key sets into the result over
+ * their union (the rescaling of the online update, Lecture 17 page §8.3,
+ * applied to partial results written back to memory, CS336 Lecture 5
+ * transcript, FlashAttention passage):
+ *   LSE = ln sum_r exp(LSE_r),   O = sum_r exp(LSE_r - LSE) O_r,
+ * with parts of LSE_r = -inf weighing nothing (all parts empty: O = 0,
+ * LSE = -inf). The same step combines the per-device results of a sequence
+ * split across devices.
+ *   o_parts    [P,B,H,N,d] float (each part normalised, O_r = o_r / l_r),
+ *              16-byte aligned.
+ *   lse_parts  [P,B,H,N] float, natural log, 4-byte aligned.
+ *   o          [B,H,N,d] output of type `dtype` (bf16: rounded once, RNE),
+ *              16-byte aligned; lse [B,H,N] float output, 4-byte aligned.
+ *              Outputs must not overlap the inputs or each other.
+ * 1 <= P <= 2^20; d in {64, 128}.
+ */
+attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t B,
+                       int64_t H, int64_t N, int64_t d, void* o, float* lse, attn_dtype dtype,
+                       void* stream);
 
 /* Bytes of device workspace attn_bwd needs for these sizes (the per-row
  * term D_i = sum_k dO_ik O_ik, one float per query row). */

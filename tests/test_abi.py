@@ -26,7 +26,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"attn_version", "attn_status_string", "attn_last_error", "attn_fwd",
-                          "attn_bwd_workspace_bytes", "attn_bwd"}
+                          "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
+                          "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd"}
     lib = ctypes.CDLL(ta.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -34,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = ta.library()
-    assert lib.attn_version() == 1
+    assert lib.attn_version() == 2
     assert lib.attn_status_string(0) == b"ATTN_OK"
     assert lib.attn_status_string(1) == b"ATTN_ERR_INVALID_ARGUMENT"
     assert lib.attn_status_string(2) == b"ATTN_ERR_UNSUPPORTED"
@@ -47,6 +48,11 @@ def test_workspace_bytes():
     assert lib.attn_bwd_workspace_bytes(2, 16, 4096, 128, 0) == 2 * 16 * 4096 * 4
     assert lib.attn_bwd_workspace_bytes(2, 16, 4096, 96, 0) == 0
     assert lib.attn_bwd_workspace_bytes(-1, 16, 4096, 128, 0) == 0
+    # split forward: fp32 O and LSE parts per split
+    assert lib.attn_fwd_ex_workspace_bytes(1, 16, 2048, 16384, 128, 1, 0) == 0
+    assert lib.attn_fwd_ex_workspace_bytes(1, 16, 2048, 16384, 128, 4, 0) == 4 * 16 * 2048 * 129 * 4
+    assert lib.attn_fwd_ex_workspace_bytes(1, 16, 2048, 16384, 128, 129, 0) == 0
+    assert lib.attn_fwd_ex_workspace_bytes(1, 16, 2048, 16384, 96, 4, 0) == 0
 
 
 # Fake, never dereferenced device addresses: validation must reject the call
@@ -96,6 +102,50 @@ def test_fwd_empty_is_noop():
     assert _fwd(q=0, k=0, v=0, o=0, lse=0, B=0) == 0
     assert _fwd(q=0, k=0, v=0, o=0, lse=0, N=0) == 0
     assert _err() == ""
+
+
+def _fwd_ex(q=A, k=A + T, v=A + 2 * T, o=A + 3 * T, lse=A + 4 * T, B=1, H=2, Nq=128, Nk=256,
+            d=64, scale=0.125, mask=0, splits=1, ws=None, ws_bytes=0, dt=0):
+    return ta.library().attn_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, mask, splits, ws,
+                                    ws_bytes, dt, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(mask=2), 1, "unknown mask"),
+    (dict(splits=-1), 1, "num_splits"),
+    (dict(splits=129), 1, "num_splits"),
+    (dict(splits=4), 1, "workspace is NULL"),
+    (dict(splits=4, ws=A + 5 * T, ws_bytes=64), 1, "workspace too small"),
+    (dict(splits=4, ws=A + T + 64, ws_bytes=1 << 22), 1, "workspace overlaps input k"),
+    (dict(splits=4, ws=A + 4 * T - 64, ws_bytes=1 << 22), 1, "overlap"),
+    (dict(Nk=-1), 1, "negative size"),
+    (dict(Nq=(1 << 23) + 1), 2, "too large"),
+    (dict(Nk=(1 << 23) + 1), 2, "too large"),
+    (dict(k=0), 1, "k is NULL"),
+    (dict(o=A + 2 * T + 4096), 1, "overlaps input v"),
+])
+def test_fwd_ex_rejects(kw, status, needle):
+    assert _fwd_ex(**kw) == status
+    assert needle in _err()
+
+
+def test_fwd_ex_empty_is_noop():
+    assert _fwd_ex(q=0, k=0, v=0, o=0, lse=0, Nq=0) == 0
+    assert _fwd_ex(q=0, k=0, v=0, o=0, lse=0, B=0, splits=8) == 0
+    assert _err() == ""
+
+
+def _merge(op=A, lp=A + T, P=3, B=1, H=2, N=128, d=64, o=A + 2 * T, lse=A + 3 * T, dt=0):
+    return ta.library().attn_merge(op, lp, P, B, H, N, d, o, lse, dt, None)
+
+
+def test_merge_rejects():
+    assert _merge(P=0) == 1 and "num_parts" in _err()
+    assert _merge(d=96) == 2
+    assert _merge(op=0) == 1 and "o_parts is NULL" in _err()
+    assert _merge(o=A + 64) == 1 and "overlaps input o_parts" in _err()
+    assert _merge(lse=A + T + 8) == 1 and "overlaps input lse_parts" in _err()
+    assert _merge(op=0, lp=0, o=0, lse=0, N=0) == 0
 
 
 def test_bwd_rejects():

@@ -1,0 +1,294 @@
+"""GPU parity of the extended forward (causal mask, N_q != N_k, key splits) and the merge.
+
+Everything goes through the C ABI (attn_fwd_ex, attn_merge) and is compared
+with the float64 CPU oracle on the same inputs: attention_forward with the
+causal reading query i sees key j iff j <= i + N_k - N_q, and merge_partials.
+Bars as for the plain forward: bf16 -> max abs error <= 2e-2 on O (and
+<= 2e-2 of the largest reference magnitude), fp32 -> <= 1e-5, LSE <= 1e-3
+absolute. Rows that see no key must come back as exactly O = 0, LSE = -inf.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import tiled_attention_17_amd as ta  # noqa: E402
+from oracle import attention_forward, merge_partials  # noqa: E402
+from tiled_attention_17_amd.workloads import EXTRA_WORKLOADS, Workload, make_inputs, to_f64  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+BF16_REL = 2e-2
+FP32_TOL = 1e-5
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ta.library()
+
+
+def _cuda(x):
+    return {k: t.cuda() for k, t in x.items()}
+
+
+def _wl(B, H, Nq, Nk, d, dtype="bf16", seed=0, q_std=1.0, causal=False):
+    return Workload(f"t_{B}_{H}_{Nq}_{Nk}_{d}_{dtype}", B, H, Nq, d, dtype, seed=seed, q_std=q_std,
+                    n_k=Nk, causal=causal)
+
+
+def _assert_o(name, got, want, tol, rel):
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    assert err <= tol, f"{name}: max abs err {err:.3e} > {tol:.1e}"
+    if rel is not None and want.size:
+        scale = float(np.max(np.abs(want)))
+        assert err <= rel * scale + 1e-6, f"{name}: max err {err:.3e} > {rel} * max|ref| {scale:.3e}"
+
+
+def _assert_lse(name, got, want):
+    empty = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), empty), f"{name}: rows without keys differ"
+    if (~empty).any():
+        err = float(np.max(np.abs(got[~empty] - want[~empty])))
+        assert err <= LSE_TOL, f"{name}: max abs err {err:.3e} > {LSE_TOL:.1e}"
+
+
+def _check(x, o, lse, scale, causal, tol, rel, heads=None, rows=None):
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    o, lse = to_f64(o), to_f64(lse)
+    heads = heads if heads is not None else list(np.ndindex(*q.shape[:2]))
+    for (b, h) in heads:
+        ro, rl = attention_forward(q[b, h], k[b, h], v[b, h], scale, causal=causal)
+        go, gl = o[b, h], lse[b, h]
+        if rows is not None:
+            ro, rl, go, gl = ro[rows], rl[rows], go[rows], gl[rows]
+        empty = np.isneginf(rl)
+        assert np.all(go[empty] == 0), f"O[{b},{h}]: rows without keys are not 0"
+        _assert_o(f"O[{b},{h}]", go, ro, tol, rel)
+        _assert_lse(f"LSE[{b},{h}]", gl, rl)
+
+
+# ---------------------------------------------------------------------------
+# causal, equal lengths: every tile configuration, ragged N, both dtypes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("waves", ["2", "4", "8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 70, 256, 777, 1100])
+def test_causal_bf16_tile_configs(N, d, waves, monkeypatch):
+    monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    w = _wl(1, 3, N, N, d, seed=N + d, q_std=2.0, causal=True)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, True, BF16_TOL, BF16_REL)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 33, 200])
+def test_causal_fp32(N, d):
+    w = _wl(1, 2, N, N, d, dtype="fp32", seed=N, causal=True)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, True, FP32_TOL, None)
+
+
+def test_causal_first_row_is_first_value():
+    w = _wl(2, 2, 300, 300, 128, seed=3, causal=True)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0], x["v"][:, :, 0])
+    want = w.scale * (x["q"][:, :, 0].double() * x["k"][:, :, 0].double()).sum(-1)
+    assert float((lse[:, :, 0].double() - want).abs().max()) <= 1e-5
+
+
+def test_causal_ignores_hidden_keys():
+    # Keys and values no query may see (all keys after the last query's
+    # window do not exist with equal lengths, so use N_q < N_k and perturb the
+    # keys hidden from the first half of the queries).
+    w = _wl(1, 2, 256, 512, 64, seed=4, causal=True)
+    x = _cuda(make_inputs(w))
+    o1, l1 = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
+    k2, v2 = x["k"].clone(), x["v"].clone()
+    first_hidden = 128 + 512 - 256  # first key hidden from query 127
+    k2[:, :, first_hidden:] = 40.0
+    v2[:, :, first_hidden:] = -7.0
+    o2, l2 = ta.attn_fwd_ex(x["q"], k2, v2, w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, :128], o2[:, :, :128]) and torch.equal(l1[:, :, :128], l2[:, :, :128])
+
+
+# ---------------------------------------------------------------------------
+# N_q != N_k, with and without the mask (N_q > N_k leaves rows with no key)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("waves", ["2", "4", "8"])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1000), (100, 700), (300, 129), (513, 64), (64, 2048)])
+def test_unequal_lengths_bf16(Nq, Nk, waves, causal, monkeypatch):
+    monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    w = _wl(2, 2, Nq, Nk, 128, seed=Nq + Nk, q_std=3.0)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, causal, BF16_TOL, BF16_REL)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_unequal_lengths_d64_and_fp32(causal):
+    w = _wl(1, 2, 150, 400, 64, seed=11)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
+    wf = _wl(1, 2, 150, 90, 64, dtype="fp32", seed=12)
+    xf = _cuda(make_inputs(wf))
+    of, lf = ta.attn_fwd_ex(xf["q"], xf["k"], xf["v"], wf.scale, causal=causal)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, causal, BF16_TOL, BF16_REL)
+    _check(xf, of, lf, wf.scale, causal, FP32_TOL, None)
+
+
+def test_no_keys_gives_empty_rows():
+    q = torch.randn(1, 2, 70, 64, device="cuda").to(torch.bfloat16)
+    kv = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = ta.attn_fwd_ex(q, kv, kv.clone())
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# ---------------------------------------------------------------------------
+# key splits (partials in the workspace, then the merge kernel)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [2, 3, 7])
+@pytest.mark.parametrize("waves", ["2", "4", "8"])
+def test_splits_bf16(splits, waves, causal, monkeypatch):
+    monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    w = _wl(1, 2, 300, 1000, 128, seed=20 + splits, q_std=2.0)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, causal, BF16_TOL, BF16_REL)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_splits_fp32_and_d64(causal):
+    w = _wl(1, 2, 40, 500, 64, dtype="fp32", seed=30)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal, num_splits=3)
+    wb = _wl(2, 1, 200, 300, 64, seed=31)
+    xb = _cuda(make_inputs(wb))
+    ob, lb = ta.attn_fwd_ex(xb["q"], xb["k"], xb["v"], wb.scale, causal=causal, num_splits=5)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, causal, FP32_TOL, None)
+    _check(xb, ob, lb, wb.scale, causal, BF16_TOL, BF16_REL)
+
+
+def test_splits_match_single_pass_closely():
+    # Same inputs, one pass vs four splits: both within the bar of the
+    # oracle, and of each other (fp32 partials, one rounding at the end).
+    w = _wl(2, 2, 64, 4096, 128, seed=40)
+    x = _cuda(make_inputs(w))
+    o1, l1 = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=1)
+    o4, l4 = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=4)
+    torch.cuda.synchronize()
+    assert float((o1.float() - o4.float()).abs().max()) <= 2 * BF16_TOL
+    assert float((l1 - l4).abs().max()) <= LSE_TOL
+    _check(x, o4, l4, w.scale, False, BF16_TOL, BF16_REL)
+
+
+def test_auto_splits_decode_shape():
+    w = _wl(4, 8, 1, 3000, 128, seed=41)
+    x = _cuda(make_inputs(w))
+    s = ta.attn_fwd_ex_auto_splits(w.B, w.H, 1, 3000, 128)
+    assert s > 1
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=0)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL)
+
+
+def test_more_splits_than_key_tiles():
+    w = _wl(1, 1, 10, 200, 64, seed=42)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=16)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL)
+
+
+# ---------------------------------------------------------------------------
+# attn_merge on its own
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
+def test_merge_against_oracle(d, out_dtype):
+    rng = np.random.default_rng(d)
+    P, B, H, N = 5, 2, 3, 77
+    o_parts = rng.standard_normal((P, B, H, N, d))
+    lse_parts = rng.standard_normal((P, B, H, N)) * 4.0 + 30.0
+    lse_parts[1, 0, 0] = -np.inf                 # an empty part
+    lse_parts[:, 1, 2, :5] = -np.inf             # rows whose parts are all empty
+    o_parts[:, 1, 2, :5] = 0.0
+    o_parts = o_parts.astype(np.float32)
+    lse_parts = lse_parts.astype(np.float32)
+    dt = torch.float32 if out_dtype == "fp32" else torch.bfloat16
+    o, lse = ta.attn_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda(), dtype=dt)
+    torch.cuda.synchronize()
+    ro, rl = merge_partials(o_parts.astype(np.float64), lse_parts.astype(np.float64))
+    go, gl = to_f64(o), to_f64(lse)
+    _assert_o("O", go, ro, FP32_TOL if out_dtype == "fp32" else BF16_TOL, None)
+    _assert_lse("LSE", gl, rl)
+    assert np.all(go[1, 2, :5] == 0)
+
+
+def test_merge_of_gpu_key_ranges_equals_whole():
+    # Sequence-split use: attention of one query block over two halves of the
+    # keys (each on the GPU, fp32 inputs for an fp32 comparison), merged on
+    # the GPU, against the oracle over all keys.
+    w = _wl(1, 2, 96, 600, 64, dtype="fp32", seed=50)
+    x = _cuda(make_inputs(w))
+    parts = [ta.attn_fwd_ex(x["q"], x["k"][:, :, a:b].contiguous(), x["v"][:, :, a:b].contiguous(), w.scale)
+             for a, b in ((0, 250), (250, 600))]
+    o_parts = torch.stack([p[0] for p in parts]).contiguous()
+    lse_parts = torch.stack([p[1] for p in parts]).contiguous()
+    o, lse = ta.attn_merge(o_parts, lse_parts, dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, False, FP32_TOL, None)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads of these paths, sampled
+# ---------------------------------------------------------------------------
+
+def test_workload_causal_full_heads_sampled():
+    w = EXTRA_WORKLOADS[0]
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, True, BF16_TOL, BF16_REL, heads=[(0, 0), (1, 15), (1, 6)])
+
+
+def test_workload_shard_rows_sampled():
+    w = EXTRA_WORKLOADS[1]
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, w.Nq - 1], rng.integers(0, w.Nq, 100)]))
+    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL, heads=[(0, 0), (0, 9), (0, 15)], rows=rows)
+
+
+def test_workload_decode_heads_sampled():
+    w = EXTRA_WORKLOADS[2]
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=0)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (7, 15), (3, 4), (5, 11)]
+    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL, heads=heads)

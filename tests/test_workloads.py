@@ -2,7 +2,7 @@
 
 import torch
 
-from tiled_attention_17_amd.workloads import WORKLOADS, BY_NAME, HEADLINE, make_inputs
+from tiled_attention_17_amd.workloads import EXTRA_WORKLOADS, WORKLOADS, BY_NAME, HEADLINE, make_inputs
 
 
 def test_table():
@@ -39,3 +39,15 @@ def test_bf16_is_rne_of_fp32_draw():
     g = torch.Generator().manual_seed(w.seed)
     q32 = torch.randn(w.shape(), generator=g)
     assert torch.equal(make_inputs(w)["q"], q32.to(torch.bfloat16))
+
+
+def test_unequal_lengths_and_causal_workloads():
+    causal, shard, decode = EXTRA_WORKLOADS
+    assert causal.causal and causal.shape() == HEADLINE.shape() and causal.Nk == causal.N
+    assert (shard.Nq, shard.Nk, shard.q_std) == (2048, 16384, 3.0)
+    assert (decode.B, decode.H, decode.Nq, decode.Nk) == (8, 16, 1, 8192)
+    x = make_inputs(shard.with_size(H=2, N=64, n_k=200))
+    assert x["q"].shape == (1, 2, 64, 128) and x["k"].shape == (1, 2, 200, 128)
+    assert x["v"].shape == x["k"].shape
+    y = make_inputs(shard.with_size(H=2, N=64, n_k=200), with_grad_output=True)
+    assert y["do"].shape == (1, 2, 64, 128) and torch.equal(x["q"], y["q"])

@@ -14,13 +14,15 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "library", "AttnError",
-           "ATTN_BF16", "ATTN_FP32", "LIB_PATH"]
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
+           "attn_merge", "attn_bwd", "attn_bwd_workspace_bytes", "library", "AttnError",
+           "ATTN_BF16", "ATTN_FP32", "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtiledattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_BF16, ATTN_FP32 = 0, 1
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
 
 _lib = None
 
@@ -50,6 +52,16 @@ def library():
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_f,
                              ctypes.c_int, c_vp]
+    lib.attn_fwd_ex_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_ex_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, ctypes.c_int]
+    lib.attn_fwd_ex_auto_splits.restype = c_i64
+    lib.attn_fwd_ex_auto_splits.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i64, ctypes.c_int]
+    lib.attn_fwd_ex.restype = ctypes.c_int
+    lib.attn_fwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_f,
+                                ctypes.c_int, c_i64, c_vp, ctypes.c_size_t, ctypes.c_int, c_vp]
+    lib.attn_merge.restype = ctypes.c_int
+    lib.attn_merge.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
+                               ctypes.c_int, c_vp]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int]
     lib.attn_bwd.restype = ctypes.c_int
@@ -121,6 +133,86 @@ def attn_fwd(q, k, v, scale=None, *, out=None, lse=None, stream=None):
     with torch.cuda.device(dev):
         st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H, N, d, float(scale), _dtype_code(q), _stream(dev, stream))
+    _check(st)
+    return out, lse
+
+
+def attn_fwd_ex_workspace_bytes(B, H, Nq, Nk, d, num_splits, dtype_code=ATTN_BF16):
+    return int(library().attn_fwd_ex_workspace_bytes(B, H, Nq, Nk, d, num_splits, dtype_code))
+
+
+def attn_fwd_ex_auto_splits(B, H, Nq, Nk, d, dtype_code=ATTN_BF16):
+    """Key splits attn_fwd_ex uses with num_splits=0 on the current device."""
+    return int(library().attn_fwd_ex_auto_splits(B, H, Nq, Nk, d, dtype_code))
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def attn_fwd_ex(q, k, v, scale=None, *, causal=False, num_splits=1, out=None, lse=None,
+                workspace=None, stream=None):
+    """O, LSE of q [B, H, Nq, d] against k, v [B, H, Nk, d] (see attn_fwd_ex in tiled_attn.h).
+
+    causal: query i sees key j iff j <= i + Nk - Nq. num_splits: 1 = one pass,
+    2..128 = that many key ranges merged afterwards, 0 = the library's choice.
+    The split workspace is allocated here unless given.
+    """
+    import torch
+    lib = library()
+    _shape4("q", q)
+    dt, dev = q.dtype, q.device
+    B, H, Nq, d = q.shape
+    _shape4("k", k, None, dt, dev)
+    Nk = k.shape[2]
+    _shape4("k", k, (B, H, Nk, d), dt, dev)
+    _shape4("v", v, (B, H, Nk, d), dt, dev)
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _shape4("out", out, (B, H, Nq, d), dt, dev)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    code = _dtype_code(q)
+    mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
+    with torch.cuda.device(dev):
+        splits = num_splits if num_splits != 0 else attn_fwd_ex_auto_splits(B, H, Nq, Nk, d, code)
+        need = attn_fwd_ex_workspace_bytes(B, H, Nq, Nk, d, splits, code)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = lib.attn_fwd_ex(q.data_ptr(), _ptr(k), _ptr(v), out.data_ptr(), lse.data_ptr(),
+                             B, H, Nq, Nk, d, float(scale), mask, splits, _ptr(workspace), ws_bytes,
+                             code, _stream(dev, stream))
+    _check(st)
+    return out, lse
+
+
+def attn_merge(o_parts, lse_parts, *, dtype=None, out=None, lse=None, stream=None):
+    """Merge fp32 partial results o_parts [P, B, H, N, d], lse_parts [P, B, H, N] (see attn_merge)."""
+    import torch
+    lib = library()
+    if o_parts.dim() != 5 or o_parts.dtype != torch.float32 or not o_parts.is_contiguous():
+        raise ValueError("o_parts must be a contiguous float32 [P, B, H, N, d] tensor")
+    P, B, H, N, d = o_parts.shape
+    if tuple(lse_parts.shape) != (P, B, H, N) or lse_parts.dtype != torch.float32 \
+            or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous float32 [P, B, H, N] tensor")
+    dev = o_parts.device
+    dtype = torch.bfloat16 if dtype is None else dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=dtype, device=dev)
+    _shape4("out", out, (B, H, N, d), dtype, dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), P, B, H, N, d, out.data_ptr(),
+                            lse.data_ptr(), _dtype_code(out), _stream(dev, stream))
     _check(st)
     return out, lse
 

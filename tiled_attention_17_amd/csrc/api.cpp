@@ -42,7 +42,10 @@ struct Range {
   uintptr_t hi;  // exclusive
 };
 
-bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+// Empty ranges overlap nothing.
+bool overlaps(const Range& a, const Range& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
 
 // Sizes shared by both entry points. Fills `elems` (elements per tensor)
 // and `rows` (B*H*N) when the shape is valid.
@@ -126,7 +129,7 @@ int env_waves() {
 
 extern "C" {
 
-int attn_version(void) { return 1; }
+int attn_version(void) { return 2; }
 
 const char* attn_status_string(attn_status status) {
   switch (status) {
@@ -140,34 +143,139 @@ const char* attn_status_string(attn_status status) {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
+}  // extern "C"
+
+namespace {
+
+// Bytes of the split-key workspace: fp32 O parts [S, B*H, Nq, d] and LSE
+// parts [S, B*H, Nq].
+size_t split_workspace_bytes(int64_t rows, int64_t d, int64_t splits) {
+  return splits > 1 ? (size_t)splits * (size_t)rows * (size_t)(d + 1) * sizeof(float) : 0;
+}
+
+attn_status fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                       int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int mask,
+                       int64_t num_splits, void* workspace, size_t workspace_bytes,
+                       attn_dtype dtype, void* stream) {
+  int64_t q_elems = 0, q_rows = 0, k_elems = 0, k_rows = 0;
+  attn_status s = check_shape(B, H, Nq, d, dtype, &q_elems, &q_rows);
+  if (s != ATTN_OK) return s;
+  if ((s = check_shape(B, H, Nk, d, dtype, &k_elems, &k_rows)) != ATTN_OK) return s;
+  if ((s = check_scale(scale)) != ATTN_OK) return s;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown mask %d", mask);
+  if (num_splits < 0 || num_splits > tattn::kMaxSplits)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "num_splits=%lld out of range (0 .. %d)",
+                (long long)num_splits, tattn::kMaxSplits);
+  if (q_rows == 0) return ok();
+  if ((s = check_ptr(q, "q", 16)) != ATTN_OK || (s = check_ptr(o, "o", 16)) != ATTN_OK ||
+      (s = check_ptr(lse, "lse", 16)) != ATTN_OK)
+    return s;
+  if (k_rows > 0 && ((s = check_ptr(k, "k", 16)) != ATTN_OK || (s = check_ptr(v, "v", 16)) != ATTN_OK))
+    return s;
+
+  int cus = 0;
+  if (num_splits == 0 && (s = device_cus(&cus)) != ATTN_OK) return s;
+  const int64_t bh = B * H;
+  int64_t splits = num_splits == 0 ? tattn::fwd_auto_splits(bh, Nq, Nk, dtype == ATTN_FP32, cus) : num_splits;
+  if (k_rows == 0) splits = 1;
+  const size_t need = split_workspace_bytes(q_rows, d, splits);
+  if (need > 0) {
+    if ((s = check_ptr(workspace, "workspace", 16)) != ATTN_OK) return s;
+    if (workspace_bytes < need)
+      return fail(ATTN_ERR_INVALID_ARGUMENT, "workspace too small for %lld key splits: %zu bytes given, %zu needed",
+                  (long long)splits, workspace_bytes, need);
+  }
+
+  const uintptr_t e = dtype == ATTN_FP32 ? 4 : 2;
+  const Range in[3] = {{"q", (uintptr_t)q, (uintptr_t)q + (uintptr_t)q_elems * e},
+                 {"k", (uintptr_t)k, (uintptr_t)k + (uintptr_t)k_elems * e},
+                 {"v", (uintptr_t)v, (uintptr_t)v + (uintptr_t)k_elems * e}};
+  const Range out[3] = {{"o", (uintptr_t)o, (uintptr_t)o + (uintptr_t)q_elems * e},
+                        {"lse", (uintptr_t)lse, (uintptr_t)lse + (uintptr_t)q_rows * 4},
+                        {"workspace", (uintptr_t)workspace, (uintptr_t)workspace + need}};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& b : in)
+      if (overlaps(out[i], b))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", out[i].name, b.name);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(out[i], out[j]))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs %s and %s overlap", out[i].name, out[j].name);
+  }
+
+  if (cus == 0 && (s = device_cus(&cus)) != ATTN_OK) return s;
+  tattn::FwdArgs a{q, k, v, o, lse, bh, Nq, Nk, d, scale, dtype == ATTN_FP32,
+                   mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves()};
+  const hipError_t he = tattn::launch_attn_fwd(a);
+  if (he != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(he));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                      int64_t H, int64_t N, int64_t d, float scale, attn_dtype dtype,
                      void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, N, d, scale, ATTN_MASK_NONE, 1, nullptr, 0, dtype,
+                    stream);
+}
+
+size_t attn_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                   int64_t num_splits, attn_dtype dtype) {
+  int64_t elems = 0, rows = 0, ke = 0, kr = 0;
+  if (check_shape(B, H, Nq, d, dtype, &elems, &rows) != ATTN_OK) return 0;
+  if (check_shape(B, H, Nk, d, dtype, &ke, &kr) != ATTN_OK) return 0;
+  if (num_splits < 0 || num_splits > tattn::kMaxSplits) return 0;
+  return split_workspace_bytes(rows, d, num_splits);
+}
+
+int64_t attn_fwd_ex_auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                attn_dtype dtype) {
+  int64_t elems = 0, rows = 0, ke = 0, kr = 0;
+  if (check_shape(B, H, Nq, d, dtype, &elems, &rows) != ATTN_OK) return 0;
+  if (check_shape(B, H, Nk, d, dtype, &ke, &kr) != ATTN_OK) return 0;
+  if (rows == 0 || kr == 0) return 1;
+  int cus = 0;
+  if (device_cus(&cus) != ATTN_OK) return 0;
+  return tattn::fwd_auto_splits(B * H, Nq, Nk, dtype == ATTN_FP32, cus);
+}
+
+attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                        attn_mask mask, int64_t num_splits, void* workspace,
+                        size_t workspace_bytes, attn_dtype dtype, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, (int)mask, num_splits, workspace,
+                    workspace_bytes, dtype, stream);
+}
+
+attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t B,
+                       int64_t H, int64_t N, int64_t d, void* o, float* lse, attn_dtype dtype,
+                       void* stream) {
   int64_t elems = 0, rows = 0;
   attn_status s = check_shape(B, H, N, d, dtype, &elems, &rows);
   if (s != ATTN_OK) return s;
-  if ((s = check_scale(scale)) != ATTN_OK) return s;
+  if (num_parts < 1 || num_parts > (int64_t(1) << 20))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "num_parts=%lld out of range (1 .. 2^20)", (long long)num_parts);
   if (rows == 0) return ok();
-  if ((s = check_ptr(q, "q", 16)) != ATTN_OK || (s = check_ptr(k, "k", 16)) != ATTN_OK ||
-      (s = check_ptr(v, "v", 16)) != ATTN_OK || (s = check_ptr(o, "o", 16)) != ATTN_OK ||
-      (s = check_ptr(lse, "lse", 16)) != ATTN_OK)
+  if ((s = check_ptr(o_parts, "o_parts", 16)) != ATTN_OK || (s = check_ptr(lse_parts, "lse_parts", 4)) != ATTN_OK ||
+      (s = check_ptr(o, "o", 16)) != ATTN_OK || (s = check_ptr(lse, "lse", 4)) != ATTN_OK)
     return s;
-  const uintptr_t tb = (uintptr_t)elems * (dtype == ATTN_FP32 ? 4 : 2);
-  const Range in[3] = {{"q", (uintptr_t)q, (uintptr_t)q + tb},
-                       {"k", (uintptr_t)k, (uintptr_t)k + tb},
-                       {"v", (uintptr_t)v, (uintptr_t)v + tb}};
-  const Range out[2] = {{"o", (uintptr_t)o, (uintptr_t)o + tb},
+  if ((uint64_t)num_parts * (uint64_t)elems > (uint64_t)INT64_MAX / 8)
+    return fail(ATTN_ERR_UNSUPPORTED, "partial results too large");
+  const uintptr_t e = dtype == ATTN_FP32 ? 4 : 2;
+  const Range in[2] = {{"o_parts", (uintptr_t)o_parts, (uintptr_t)o_parts + (uintptr_t)(num_parts * elems) * 4},
+                       {"lse_parts", (uintptr_t)lse_parts, (uintptr_t)lse_parts + (uintptr_t)(num_parts * rows) * 4}};
+  const Range out[2] = {{"o", (uintptr_t)o, (uintptr_t)o + (uintptr_t)elems * e},
                         {"lse", (uintptr_t)lse, (uintptr_t)lse + (uintptr_t)rows * 4}};
   for (const Range& a : out)
     for (const Range& b : in)
       if (overlaps(a, b)) return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", a.name, b.name);
   if (overlaps(out[0], out[1])) return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs o and lse overlap");
-
-  int cus = 0;
-  if ((s = device_cus(&cus)) != ATTN_OK) return s;
-  tattn::FwdArgs a{q, k, v, o, lse, B * H, N, d, scale, dtype == ATTN_FP32, stream, cus, env_waves()};
-  const hipError_t e = tattn::launch_attn_fwd(a);
-  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  const hipError_t he = tattn::launch_attn_merge(o_parts, lse_parts, (int)num_parts, rows, d, o, lse,
+                                                 dtype == ATTN_FP32, stream);
+  if (he != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(he));
   return ok();
 }
 

@@ -119,6 +119,12 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
 // softmax as with the running max itself.
 constexpr float kLazyRescale = 8.0f;
 
+// Most key tiles of one query tile that need a mask: with BN-key tiles and
+// BM queries, the keys seen by some but not all queries of the tile span at
+// most BM - 1 positions, which touch at most ceil((BN - 1 + BM - 1) / BN)
+// tiles: 3 for (BM, BN) = (256, 128), (128, 64) and fewer for (64, 64).
+constexpr int kMaxMaskedTiles = 3;
+
 // Per-lane element offsets of the V^T operand reads: the A operand of step t,
 // d block db (rows d = 32 db + lq, keys 16 t + 8 h .. + 7) sits in sub-tile
 // t / 4 at o[(t % 4) ^ db] + db * 32 * 64. With d = 32 db + lq,
@@ -177,19 +183,23 @@ __device__ __forceinline__ void score_tile(const bf16* kt, const bf16x8* qf,
 }
 
 // Online softmax update (Lecture 17 page, §8.3) for the query this lane owns,
-// over one 64-key tile whose first key is key0. Produces P (bf16, packed in
+// over one key tile whose first key is key0. Produces P (bf16, packed in
 // the B-operand order of the value product), updates the running (m, l) and
 // rescales the output accumulator by alpha when the running max moves.
-template <bool RAGGED, int DB, int NKB = 2>
-__device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, int N, int h,
+// MASKED tiles drop keys past kmax, the last key this lane's query may see
+// (the end of the key range, or of its causal window): p = 0 for them. A row
+// that has not seen a visible key yet keeps m = -inf, l = 0, o = 0 (its
+// exponentials are taken against 0 instead of -inf).
+template <bool MASKED, int DB, int NKB = 2>
+__device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, int kmax, int h,
                                              float& m_run, float& l_run, f32x16* oacc,
                                              u32x4* pw) {
-  if (RAGGED) {
+  if (MASKED) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key0 + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7) >= N) sacc[kb][i] = -INFINITY;
+        if (key0 + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7) > kmax) sacc[kb][i] = -INFINITY;
   }
   float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
@@ -197,9 +207,10 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
 #pragma unroll
     for (int i = (kb < 2 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
   mx = max_with_other_half(mx);
-  const float mt = mx * c;
+  const float mt = (MASKED && mx == -INFINITY) ? -INFINITY : mx * c;
   const float m_new = mt > m_run + kLazyRescale ? mt : m_run;
-  const float alpha = fast_exp2(m_run - m_new);
+  const float m_ref = (MASKED && m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(m_run - m_ref);
   // The row sum adds the fp32 p (the sum of the bf16-rounded operands would
   // put up to 2^-9 relative error into LSE when a few keys dominate a row).
   float ls0 = 0.f, ls1 = 0.f;
@@ -207,9 +218,9 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      float p0 = fast_exp2(fmaf(sacc[kb][i], c, -m_new));
-      float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_new));
-      if (RAGGED) {
+      float p0 = fast_exp2(fmaf(sacc[kb][i], c, -m_ref));
+      float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_ref));
+      if (MASKED) {
         p0 = sacc[kb][i] == -INFINITY ? 0.f : p0;
         p1 = sacc[kb][i + 1] == -INFINITY ? 0.f : p1;
       }
@@ -311,23 +322,115 @@ __device__ __forceinline__ void mfma_phase(const bf16* kt, const bf16* vt, const
   }
 }
 
-// Epilogue: O = o / l (bf16), LSE = ln 2 (m + log2 l).
-template <int D>
+// Epilogue: O = o / l, LSE = ln 2 (m + log2 l), as bf16 (final result) or
+// fp32 (PARTIAL: the result over one key range, merged later). A row that
+// saw no visible key has l = 0 and m = -inf: O = 0, LSE = -inf.
+template <int D, bool PARTIAL>
 __device__ __forceinline__ void store_output(const f32x16* oacc, float m_run, float l_run,
-                                             bf16* orow, float* lse, bool q_ok, int h) {
+                                             void* orow, float* lse, bool q_ok, int h) {
   const float l_tot = add_other_half(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!q_ok) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[db][4 * r + 0] * inv, oacc[db][4 * r + 1] * inv);
-      w[1] = pack_bf16x2(oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv);
-      *(u32x2*)(orow + 32 * db + 8 * r + 4 * h) = w;
+      if (PARTIAL) {
+        const f32x4 w = {oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv, oacc[db][4 * r + 2] * inv,
+                         oacc[db][4 * r + 3] * inv};
+        *(f32x4*)((float*)orow + 32 * db + 8 * r + 4 * h) = w;
+      } else {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * r + 0] * inv, oacc[db][4 * r + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv);
+        *(u32x2*)((bf16*)orow + 32 * db + 8 * r + 4 * h) = w;
+      }
     }
   if (h == 0) *lse = (m_run + fast_log2(l_tot)) * kLn2;
+}
+
+// Workgroup -> (head, query tile, key split). Causal launches put the query
+// tiles that see the most keys first (consecutive workgroups take one query
+// tile of every head and split, and the dispatcher starts them in order), so
+// the short tiles fill in behind the long ones; other launches keep the query
+// tiles of one head (which share K and V) on one XCD.
+struct TileId {
+  int bh, qt, split;
+};
+__device__ __forceinline__ TileId decode_tile(const FwdParams& p) {
+  TileId t;
+  int rest;
+  if (p.causal) {
+    const int hs = p.BH * p.n_splits;
+    const int r = (int)blockIdx.x / hs;
+    rest = (int)blockIdx.x - r * hs;
+    t.qt = p.n_qtiles - 1 - r;
+  } else {
+    const int w = xcd_tile(blockIdx.x, p.total_tiles, p.remap);
+    rest = w / p.n_qtiles;
+    t.qt = w - rest * p.n_qtiles;
+  }
+  t.bh = rest / p.n_splits;
+  t.split = rest - t.bh * p.n_splits;
+  // The divisions above run on the vector unit; marking the results
+  // wave-uniform keeps every address derived from them in scalar registers
+  // (else each buffer_load ... lds would sit in a readfirstlane loop).
+  t.bh = __builtin_amdgcn_readfirstlane(t.bh);
+  t.qt = __builtin_amdgcn_readfirstlane(t.qt);
+  t.split = __builtin_amdgcn_readfirstlane(t.split);
+  return t;
+}
+
+// Keys one workgroup visits: the split's range [k_begin, k_end), cut short
+// by the causal window of its last query (query i sees keys
+// j <= i + Nk - Nq). n_tiles key tiles of BN keys hold a key some query of
+// the tile sees; the first n_full of them are seen in full by every query of
+// the tile and need no mask.
+struct KeyRange {
+  int k_begin, k_end, n_tiles, n_full;
+};
+template <int BN>
+__device__ __forceinline__ KeyRange key_range(const FwdParams& p, int split, int q_lo, int bm) {
+  KeyRange r;
+  r.k_begin = split * p.split_keys;
+  r.k_end = min(p.Nk, r.k_begin + p.split_keys);
+  const int off = p.Nk - p.Nq;
+  const int q_hi = min(q_lo + bm, p.Nq) - 1;
+  const int lim = p.causal ? min(r.k_end, q_hi + off + 1) : r.k_end;
+  r.n_tiles = lim > r.k_begin ? (lim - r.k_begin + BN - 1) / BN : 0;
+  const int seen_by_all = (p.causal ? min(r.k_end, q_lo + off + 1) : r.k_end) - r.k_begin;
+  r.n_full = seen_by_all > 0 ? seen_by_all / BN : 0;
+  return r;
+}
+// Last key of the range that query q_row sees.
+__device__ __forceinline__ int row_kmax(const FwdParams& p, const KeyRange& r, int q_row) {
+  return p.causal ? min(r.k_end - 1, q_row + p.Nk - p.Nq) : r.k_end - 1;
+}
+
+// Writes one wave's rows: O and LSE, or the fp32 partial of the key split.
+template <int D>
+__device__ __forceinline__ void write_result(const FwdParams& p, const TileId& t, int q_row,
+                                             bool q_ok, int h, const f32x16* oacc, float m_run,
+                                             float l_run) {
+  if (p.n_splits > 1) {
+    const size_t row = ((size_t)t.split * p.BH + t.bh) * p.Nq + q_row;
+    store_output<D, true>(oacc, m_run, l_run, p.o_part + row * D, p.lse_part + row, q_ok, h);
+  } else {
+    const size_t row = (size_t)t.bh * p.Nq + q_row;
+    store_output<D, false>(oacc, m_run, l_run, (bf16*)p.o + row * D, p.lse + row, q_ok, h);
+  }
+}
+
+// Result of a query tile none of whose queries sees a key of the range.
+template <int D>
+__device__ __forceinline__ void write_empty(const FwdParams& p, const TileId& t, int q_row,
+                                            bool q_ok, int h) {
+  f32x16 z[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[db][i] = 0.f;
+  write_result<D>(p, t, q_row, q_ok, h, z, -INFINITY, 0.f);
 }
 
 // Q^T as the B operand: lane (query lq, half h) holds d = 16 s + 8 h .. +7.
@@ -434,16 +537,18 @@ struct Stager {
 // lane-linearly (lane L -> 16 bytes at L * 16), and each lane loads the
 // global chunk that belongs there in the swizzled layout (LDS row r holds
 // key swap23(r), chunk position p holds logical chunk p ^ kswz(r)). The
-// per-lane byte offsets within a tile are fixed, the tile's base goes in the
-// scalar offset, so staging a tile costs no VALU work. Rows >= N read as
-// zeros (buffer range check). Completion is waited for with vmcnt before
-// the barrier that publishes the tile.
+// per-lane byte offsets within a tile are fixed; each tile gets a buffer
+// resource of its own that starts at the tile's first row and ends at the
+// head's last row, so rows >= N read as zeros through the range check of
+// the per-lane offset (the scalar offset stays 0), and staging a tile costs
+// no VALU work. Completion is waited for with vmcnt before the barrier that
+// publishes the tile.
 // One buffer_load_dwordx4 ... lds: 16 bytes per lane from byte offset
-// voff + soff of the buffer to LDS address lds + 16 * lane. (A plain device
+// voff of the buffer to LDS address lds + 16 * lane. (A plain device
 // function: the host pass of a kernel template must not see the builtin.)
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff, int soff) {
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
-                                           soff, 0, 0);
+                                           0, 0, 0);
 }
 
 template <int D, int ROWS, int WAVES = 4>
@@ -463,10 +568,15 @@ struct KDirect {
       voff[i] = (swap23(lr) * D + 8 * c) * 2;
     }
   }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, int tile, int bn, bf16* kt) const {
-    const int soff = tile * bn * D * 2;
+  // Tile `tile` (rows tile * bn ..) of a head whose K rows start at kbase
+  // and number n_rows.
+  __device__ __forceinline__ void load(const bf16* kbase, int n_rows, int tile, int bn, bf16* kt) const {
+    const int row0 = tile * bn;
+    const int rem = n_rows > row0 ? n_rows - row0 : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (size_t)row0 * D), 0, rem * D * 2, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lds_dma16(kr, kt + (lds_row0 + i * RPI) * D, voff[i], soff);
+    for (int i = 0; i < NI; ++i) lds_dma16(r, kt + (lds_row0 + i * RPI) * D, voff[i]);
   }
 };
 
@@ -485,30 +595,33 @@ __device__ __forceinline__ void phase_barrier() {
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 2)))
-void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                          const bf16* __restrict__ V, bf16* __restrict__ O,
-                          float* __restrict__ LSE, int N, int n_qtiles, int total_tiles, float c,
-                          int remap) {
+void attn_fwd_bf16_kernel(const FwdParams p) {
   using T = FwdTile<D>;
   constexpr int BM = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::STAGE];
   auto ks = [&](int b) { return smem + b * T::STAGE; };
   auto vs = [&](int b) { return smem + b * T::STAGE + T::KTILE; };
 
-  const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
-  const int bh = tile / n_qtiles;
-  const int qt = tile - bh * n_qtiles;
-  const size_t base = (size_t)bh * N * D;
-  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(K + base, N);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<D>(V + base, N);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
-  const int q_row = qt * BM + wave * 32 + lq;
-  const bool q_ok = q_row < N;
+  const TileId ti = decode_tile(p);
+  const bf16* Kh = (const bf16*)p.k + (size_t)ti.bh * p.Nk * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(Kh, p.Nk);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<D>((const bf16*)p.v + (size_t)ti.bh * p.Nk * D, p.Nk);
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addresses
+  const int q_row = ti.qt * BM + wave * 32 + lq;
+  const bool q_ok = q_row < p.Nq;
+  const KeyRange kr = key_range<T::BN>(p, ti.split, ti.qt * BM, BM);
+  if (kr.n_tiles == 0) {
+    write_empty<D>(p, ti, q_row, q_ok, h);
+    return;
+  }
+  const int t0 = kr.k_begin / T::BN;  // first key tile of the range
+  const int kmax = row_kmax(p, kr, q_row);
   const VtOffsets vo(lq, h);
   const KOffsets<D, true> ko(lq, h);
 
   bf16x8 qf[T::DK];
-  load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
+  load_q<D>((const bf16*)p.q + ((size_t)ti.bh * p.Nq + q_row) * D, q_ok, h, qf);
 
   f32x16 oacc[T::DB];
 #pragma unroll
@@ -517,46 +630,50 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int n_kt = (N + T::BN - 1) / T::BN;
+  const int n_kt = kr.n_tiles;
   // The next tile's K goes straight to LDS; its V is staged through
   // registers in two halves of 32 rows (the first half's loads overlap the
   // score product and softmax, the second half's the value product).
   const KDirect<D, 64, NW> kd(0, wave, lane);
   Stager<D, 32, NW * 64, 64, false> st;
-  kd.load(krs, 0, 64, ks(0));
+  kd.load(Kh, p.Nk, t0, 64, ks(0));
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    st.load(krs, vrs, 0, 0, 32 * half, tid);
+    st.load(krs, vrs, t0, t0, 32 * half, tid);
     st.store(ks(0), vs(0), 32 * half, tid);
   }
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_kt; ++j) {
+  auto step = [&](auto masked, int j) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = j & 1;
     const bool more = j + 1 < n_kt;
     if (more) {
-      kd.load(krs, j + 1, 64, ks(cur ^ 1));
-      st.load(krs, vrs, j + 1, j + 1, 0, tid);
+      kd.load(Kh, p.Nk, t0 + j + 1, 64, ks(cur ^ 1));
+      st.load(krs, vrs, t0 + j + 1, t0 + j + 1, 0, tid);
     }
     f32x16 sacc[2];
     u32x4 pw[4];
     score_tile<D>(ks(cur), qf, ko, sacc);
-    if ((j + 1) * T::BN > N)
-      softmax_tile<true, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
-    else
-      softmax_tile<false, T::DB>(sacc, c, j * T::BN, N, h, m_run, l_run, oacc, pw);
+    softmax_tile<MASKED, T::DB>(sacc, p.c, kr.k_begin + j * T::BN, kmax, h, m_run, l_run, oacc, pw);
     if (more) {
       st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
-      st.load(krs, vrs, j + 1, j + 1, 32, tid);
+      st.load(krs, vrs, t0 + j + 1, t0 + j + 1, 32, tid);
     }
     pv_tile<D>(vs(cur), pw, vo, oacc);
     if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 32, tid);
     wait_vmem();  // K tile written to LDS
     __syncthreads();
-  }
-  store_output<D>(oacc, m_run, l_run, O + base + (size_t)q_row * D, LSE + (size_t)bh * N + q_row,
-                  q_ok, h);
+  };
+  // Tiles from n_full on are masked; there are at most kMaxMaskedTiles.
+  const int n_plain = min(kr.n_full, n_kt);
+  int j = 0;
+  for (; j < n_plain; ++j) step(std::false_type{}, j);
+#pragma unroll
+  for (int m = 0; m < kMaxMaskedTiles; ++m)
+    if (j < n_kt) step(std::true_type{}, j++);
+  write_result<D>(p, ti, q_row, q_ok, h, oacc, m_run, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -574,10 +691,7 @@ void attn_fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 // ---------------------------------------------------------------------------
 template <int D, int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                                   const bf16* __restrict__ V, bf16* __restrict__ O,
-                                   float* __restrict__ LSE, int N, int n_qtiles, int total_tiles,
-                                   float c, int remap) {
+void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
   using T = FwdTile<D, BN>;
   constexpr int BM = 256;
   // With 64-key tiles each group issues the global loads of its staging
@@ -594,27 +708,35 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   auto ks = [&](int b) { return smem + (b & 1) * T::STAGE; };
   auto vs = [&](int b) { return smem + (b & 1) * T::STAGE + T::KTILE; };
 
-  const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
-  const int bh = tile / n_qtiles;
-  const int qt = tile - bh * n_qtiles;
-  const size_t base = (size_t)bh * N * D;
-  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(K + base, N);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<D>(V + base, N);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const TileId ti = decode_tile(p);
+  const bf16* Kh = (const bf16*)p.k + (size_t)ti.bh * p.Nk * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(Kh, p.Nk);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<D>((const bf16*)p.v + (size_t)ti.bh * p.Nk * D, p.Nk);
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addresses
   const int grp = wave >> 2;          // 0: group A, 1: group B
   const int gtid = tid & 255;         // thread index within the group
   const int r0 = (BN / 2) * grp;      // rows of each tile this group stages
-  const int q_row = qt * BM + wave * 32 + lq;
-  const bool q_ok = q_row < N;
+  const int q_row = ti.qt * BM + wave * 32 + lq;
+  const bool q_ok = q_row < p.Nq;
+  const KeyRange kr = key_range<BN>(p, ti.split, ti.qt * BM, BM);
+  if (kr.n_tiles == 0) {
+    write_empty<D>(p, ti, q_row, q_ok, h);
+    return;
+  }
+  // Key tiles are numbered from the range's first (t0 + local index); the
+  // LDS buffers alternate with the local index.
+  const int t0 = kr.k_begin / BN;
+  const int kmax = row_kmax(p, kr, q_row);
   const VtOffsets vo(lq, h);
   const KOffsets<D> ko(lq, h);
   const KDirect<D, BN / 2> kd(r0, wave & 3, lane);
-  auto stage_k = [&](int t) {  // this group's rows of K tile t (direct mode)
-    if (kDirectK) kd.load(krs, t, BN, ks(t));
+  auto stage_k = [&](int t) {  // this group's rows of local K tile t (direct mode)
+    if (kDirectK) kd.load(Kh, p.Nk, t0 + t, BN, ks(t));
   };
 
   bf16x8 qf[T::DK];
-  load_q<D>(Q + base + (size_t)q_row * D, q_ok, h, qf);
+  load_q<D>((const bf16*)p.q + ((size_t)ti.bh * p.Nq + q_row) * D, q_ok, h, qf);
 
   f32x16 oacc[T::DB];
 #pragma unroll
@@ -622,14 +744,13 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int n_kt = (N + T::BN - 1) / T::BN;
-  const bool ragged_tail = (N % T::BN) != 0;
+  const int n_kt = kr.n_tiles;
 
   {  // prologue: everyone stages K_0, V_0 and K_1
     Stager<D, BN, 512, BN> st0;
-    st0.load(krs, vrs, 0, 0, 0, tid);
+    st0.load(krs, vrs, t0, t0, 0, tid);
     st0.store(ks(0), vs(0), 0, tid);
-    st0.load(krs, vrs, 1, 1, 0, tid);
+    st0.load(krs, vrs, t0 + 1, t0 + 1, 0, tid);
     st0.store(ks(1), vs(1), 0, tid);  // V_1 rows are restaged below; K_1 is final
   }
   __syncthreads();
@@ -639,8 +760,8 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   u32x4 pw[T::NT];
   bf16x8 pre[kPrefetch];  // first V^T operands of the next MFMA phase
   // Group A stages (K_{j+2}, V_{j+1}) in VALU phase j, group B (K_{j+3}, V_{j+2}).
-  // Tiles past the end are zero-filled without memory traffic into buffers
-  // no wave reads any more.
+  // Tiles past the end of the head are zero-filled without memory traffic;
+  // tiles past the end of the range go into buffers no wave reads any more.
   StG st;
 
   // MFMA phase of tile 0: scores only
@@ -648,22 +769,22 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
   phase_barrier();
   if (grp == 1) {  // VALU phase "j = -1"
     stage_k(2);
-    st.load(krs, vrs, 2, 1, r0, gtid);
+    st.load(krs, vrs, t0 + 2, t0 + 1, r0, gtid);
   }
-  if (n_kt == 1 && ragged_tail)
-    softmax_tile<true, T::DB, T::NKB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
+  if (kr.n_full == 0)
+    softmax_tile<true, T::DB, T::NKB>(sacc, p.c, kr.k_begin, kmax, h, m_run, l_run, oacc, pw);
   else
-    softmax_tile<false, T::DB, T::NKB>(sacc, c, 0, N, h, m_run, l_run, oacc, pw);
+    softmax_tile<false, T::DB, T::NKB>(sacc, p.c, kr.k_begin, kmax, h, m_run, l_run, oacc, pw);
   if (grp == 1) st.store(ks(2), vs(1), r0, gtid);
   prefetch_pv<D, BN>(vs(0), vo, pre);
   if (kDirectK) wait_vmem();
   phase_barrier();
 
-  auto body = [&](auto ragged, int j) {
-    constexpr bool RAGGED = decltype(ragged)::value;
+  auto body = [&](auto masked, int j) {
+    constexpr bool MASKED = decltype(masked)::value;
     // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1.
     const int tk = j + 2 + grp, tv = j + 1 + grp;
-    if (kEarlyLoads) st.load(krs, vrs, tk, tv, r0, gtid);
+    if (kEarlyLoads) st.load(krs, vrs, t0 + tk, t0 + tv, r0, gtid);
     mfma_phase<D, BN, kEarlyLoads ? NVMEM : 0>(ks(j + 1), vs(j), qf, pw, vo, ko, pre, sacc, oacc);
     phase_barrier();
     // VALU phase: staging of later tiles (with early loads first, so that
@@ -673,31 +794,34 @@ void attn_fwd_bf16_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __res
       st.store(ks(tk), vs(tv), r0, gtid);
     } else {
       stage_k(tk);
-      st.load(krs, vrs, tk, tv, r0, gtid);
+      st.load(krs, vrs, t0 + tk, t0 + tv, r0, gtid);
     }
-    softmax_tile<RAGGED, T::DB, T::NKB>(sacc, c, (j + 1) * T::BN, N, h, m_run, l_run, oacc, pw);
+    softmax_tile<MASKED, T::DB, T::NKB>(sacc, p.c, kr.k_begin + (j + 1) * BN, kmax, h, m_run, l_run,
+                                        oacc, pw);
     if (!kEarlyLoads) st.store(ks(tk), vs(tv), r0, gtid);
     prefetch_pv<D, BN>(vs(j + 1), vo, pre);
     if (kDirectK) wait_vmem();  // K tile written to LDS
     phase_barrier();
   };
-  // bodies j = 0 .. n_kt - 2; only the one that takes the softmax of a
-  // ragged last tile masks keys.
+  // bodies j = 0 .. n_kt - 2 (body j takes the softmax of tile j + 1); the
+  // tiles from n_full on hold keys some query may not see and are masked.
+  // There are at most kMaxMaskedTiles of them (a 256-query tile's causal
+  // window edge spans at most 255 keys, i.e. three 128-key tiles; a ragged
+  // end adds no tile), so the masked bodies are unrolled: a loop of them
+  // beside the loop of plain bodies would not fit the register file.
   const int n_body = n_kt - 1;
-  const int n_plain = ragged_tail ? n_body - 1 : n_body;
+  const int n_plain = min(max(kr.n_full - 1, 0), n_body);
   int j = 0;
   for (; j < n_plain; ++j) body(std::false_type{}, j);
-  if (j < n_body) {
-    body(std::true_type{}, j);
-    ++j;
-  }
+#pragma unroll
+  for (int m = 0; m < kMaxMaskedTiles; ++m)
+    if (j < n_body) body(std::true_type{}, j++);
   // last tile: value product only
   mfma_phase<D, BN, 0, false>(ks(j), vs(j), qf, pw, vo, ko, pre, sacc, oacc);
   phase_barrier();
   phase_barrier();
   if (grp == 0) phase_barrier();
-  store_output<D>(oacc, m_run, l_run, O + base + (size_t)q_row * D, LSE + (size_t)bh * N + q_row,
-                  q_ok, h);
+  write_result<D>(p, ti, q_row, q_ok, h, oacc, m_run, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -717,23 +841,26 @@ struct FwdF32Cfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, float c) {
+__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const FwdParams p) {
   using C = FwdF32Cfg<D>;
   __shared__ float kt[C::BN * C::KPITCH];
   __shared__ float vt[C::BN * C::VPITCH];
 
-  const int bh = blockIdx.x / n_qtiles;
-  const int qt = blockIdx.x - bh * n_qtiles;
-  const size_t base = (size_t)bh * N * D;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
-  const int q_row = qt * C::BM + wave * C::R + lq;
-  const bool q_ok = q_row < N;
+  const TileId ti = decode_tile(p);
+  const size_t kbase = (size_t)ti.bh * p.Nk * D;
+  const float* K = (const float*)p.k;
+  const float* V = (const float*)p.v;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addresses
+  const int q_row = ti.qt * C::BM + wave * C::R + lq;
+  const bool q_ok = q_row < p.Nq;
+  const KeyRange kr = key_range<C::BN>(p, ti.split, ti.qt * C::BM, C::BM);
+  const int kmax = row_kmax(p, kr, q_row);
 
   float qf[C::DK];  // lane (query lq, half h) holds Q[q][2 s + h]
+  const float* qrow = (const float*)p.q + ((size_t)ti.bh * p.Nq + q_row) * D;
 #pragma unroll
-  for (int s = 0; s < C::DK; ++s) qf[s] = q_ok ? Q[base + (size_t)q_row * D + 2 * s + h] : 0.f;
+  for (int s = 0; s < C::DK; ++s) qf[s] = q_ok ? qrow[2 * s + h] : 0.f;
 
   f32x16 oacc[C::DB];
 #pragma unroll
@@ -742,13 +869,13 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int n_kt = (N + C::BN - 1) / C::BN;
-  for (int j = 0; j < n_kt; ++j) {
+  for (int j = 0; j < kr.n_tiles; ++j) {
+    const int key0 = kr.k_begin + j * C::BN;
     for (int e = tid; e < C::BN * D; e += C::THREADS) {
-      const int row = e / D, col = e % D, key = j * C::BN + row;
-      const bool ok = key < N;
-      kt[row * C::KPITCH + col] = ok ? K[base + (size_t)key * D + col] : 0.f;
-      vt[row * C::VPITCH + col] = ok ? V[base + (size_t)key * D + col] : 0.f;
+      const int row = e / D, col = e % D, key = key0 + row;
+      const bool ok = key < p.Nk;
+      kt[row * C::KPITCH + col] = ok ? K[kbase + (size_t)key * D + col] : 0.f;
+      vt[row * C::VPITCH + col] = ok ? V[kbase + (size_t)key * D + col] : 0.f;
     }
     __syncthreads();
 
@@ -758,25 +885,28 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
 #pragma unroll
     for (int s = 0; s < C::DK; ++s) sacc = mfma32x32x2f32(kt[lq * C::KPITCH + 2 * s + h], qf[s], sacc);
 
-    // key of slot i: j*32 + 8 (i/4) + 4 h + i%4
-    const bool ragged = (j + 1) * C::BN > N;
-    if (ragged) {
+    // key of slot i: key0 + 8 (i/4) + 4 h + i%4; keys past kmax are dropped
+    const bool masked = j >= kr.n_full;
+    if (masked) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (j * C::BN + 8 * (i >> 2) + 4 * h + (i & 3) >= N) sacc[i] = -INFINITY;
+        if (key0 + 8 * (i >> 2) + 4 * h + (i & 3) > kmax) sacc[i] = -INFINITY;
     }
     float mx = sacc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
     mx = max_with_other_half(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = fast_exp2(m_run - m_new);
-    float p[16], lsum = 0.f;
+    // A row with no visible key so far keeps m = -inf, l = 0, o = 0.
+    const float mt = mx == -INFINITY ? -INFINITY : mx * p.c;
+    const float m_new = fmaxf(m_run, mt);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    float pr[16], lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = fast_exp2(fmaf(sacc[i], c, -m_new));
-      if (ragged && sacc[i] == -INFINITY) p[i] = 0.f;
-      lsum += p[i];
+      pr[i] = fast_exp2(fmaf(sacc[i], p.c, -m_ref));
+      if (masked && sacc[i] == -INFINITY) pr[i] = 0.f;
+      lsum += pr[i];
     }
     l_run = fmaf(alpha, l_run, lsum);
     m_run = m_new;
@@ -790,15 +920,18 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
       const int key = 8 * (s >> 2) + 4 * h + (s & 3);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        oacc[db] = mfma32x32x2f32(vt[key * C::VPITCH + 32 * db + lq], p[s], oacc[db]);
+        oacc[db] = mfma32x32x2f32(vt[key * C::VPITCH + 32 * db + lq], pr[s], oacc[db]);
     }
     __syncthreads();
   }
 
   const float l_tot = add_other_half(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
-    float* orow = O + base + (size_t)q_row * D;
+    const bool part = p.n_splits > 1;
+    const size_t row = part ? ((size_t)ti.split * p.BH + ti.bh) * p.Nq + q_row
+                            : (size_t)ti.bh * p.Nq + q_row;
+    float* orow = (part ? p.o_part : (float*)p.o) + row * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -807,8 +940,52 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
                    oacc[db][4 * r + 3] * inv};
         *(f32x4*)(orow + 32 * db + 8 * r + 4 * h) = w;
       }
-    if (h == 0) LSE[(size_t)bh * N + q_row] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (h == 0) (part ? p.lse_part : p.lse)[row] = (m_run + fast_log2(l_tot)) * kLn2;
   }
+}
+
+// ---------------------------------------------------------------------------
+// merge of key-split partial results
+// ---------------------------------------------------------------------------
+// For each row: LSE = ln sum_r e^(LSE_r), O = sum_r e^(LSE_r - LSE) O_r, with
+// the largest LSE_r subtracted first; parts with LSE_r = -inf weigh 0 and a
+// row whose parts are all empty gets O = 0, LSE = -inf. This is the
+// rescaling of the online update (Lecture 17 page §8.3) applied to partial
+// results written back to memory (CS336 Lecture 5 transcript, FlashAttention
+// passage). One row per D / 4 threads, 16-byte accesses; memory-bound.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ o_part,
+                                                         const float* __restrict__ lse_part,
+                                                         int n_parts, int64_t rows,
+                                                         void* __restrict__ o,
+                                                         float* __restrict__ lse) {
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int part = threadIdx.x % TPR;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int r = 0; r < n_parts; ++r) mx = fmaxf(mx, lse_part[r * rows + row]);
+  const float shift = mx == -INFINITY ? 0.f : mx;
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < n_parts; ++r) {
+    const float w = expf(lse_part[r * rows + row] - shift);  // 0 for an empty part
+    const f32x4 x = *(const f32x4*)(o_part + ((size_t)r * rows + row) * D + 4 * part);
+    wsum += w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (OUT_F32) {
+    const f32x4 y = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *(f32x4*)((float*)o + row * D + 4 * part) = y;
+  } else {
+    u32x2 y;
+    y[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    y[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *(u32x2*)((bf16*)o + row * D + 4 * part) = y;
+  }
+  if (part == 0) lse[row] = wsum > 0.f ? shift + logf(wsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -817,37 +994,58 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
 // Keys per ping-pong phase: 128 halves the number of phases (and so the
 // per-phase cost of barriers and of refilling the operand pipeline).
 constexpr int kPingPongBN = 128;
+constexpr int kSplitAlign = 128;  // split boundaries fall on whole key tiles of every kernel
+
+int64_t split_keys_for(int64_t Nk, int n_splits) {
+  const int64_t tiles = (Nk + kSplitAlign - 1) / kSplitAlign;
+  const int64_t per = (tiles + n_splits - 1) / n_splits;
+  return (per > 0 ? per : 1) * kSplitAlign;
+}
+
+static FwdParams make_params(const FwdArgs& a, int bm, int64_t* total_out) {
+  FwdParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.Nq = (int)a.Nq;
+  p.Nk = (int)a.Nk;
+  p.BH = (int)a.BH;
+  p.n_qtiles = (int)((a.Nq + bm - 1) / bm);
+  const int64_t sk = a.n_splits > 1 ? split_keys_for(a.Nk, a.n_splits) : 0;
+  p.n_splits = a.n_splits > 1 ? (int)((a.Nk + sk - 1) / sk) : 1;
+  p.split_keys = a.n_splits > 1 ? (int)sk : (int)(((a.Nk + kSplitAlign - 1) / kSplitAlign) * kSplitAlign);
+  if (p.split_keys == 0) p.split_keys = kSplitAlign;
+  if (p.n_splits > 1) {
+    p.o_part = a.partial;
+    p.lse_part = a.partial + (size_t)p.n_splits * a.BH * a.Nq * a.d;
+  }
+  const int64_t total = (int64_t)a.BH * p.n_qtiles * p.n_splits;
+  p.total_tiles = (int)total;
+  p.c = a.scale * kLog2e;
+  p.causal = a.causal ? 1 : 0;
+  p.remap = (!a.causal && total % 8 == 0) ? 1 : 0;
+  *total_out = total;
+  return p;
+}
 
 template <int D, int NW>
-static hipError_t launch_bf16(const FwdArgs& a) {
-  constexpr int BM = 32 * NW;
-  const int n_qtiles = (int)((a.N + BM - 1) / BM);
-  const int64_t total = (int64_t)a.BH * n_qtiles;
-  if (total > INT32_MAX) return hipErrorInvalidValue;
-  const int remap = (total % 8 == 0) ? 1 : 0;
+static hipError_t launch_bf16(const FwdArgs& a, const FwdParams& p, int64_t total) {
   if constexpr (NW == 8) {
     hipLaunchKernelGGL((attn_fwd_bf16_pingpong_kernel<D, kPingPongBN>), dim3((unsigned)total), dim3(512), 0,
-                       (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, (bf16*)a.o, a.lse, (int)a.N, n_qtiles, (int)total,
-                       a.scale * kLog2e, remap);
+                       (hipStream_t)a.stream, p);
   } else {
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0,
-                       (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, (bf16*)a.o, a.lse, (int)a.N, n_qtiles, (int)total,
-                       a.scale * kLog2e, remap);
+                       (hipStream_t)a.stream, p);
   }
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_f32(const FwdArgs& a) {
-  using C = FwdF32Cfg<D>;
-  const int n_qtiles = (int)((a.N + C::BM - 1) / C::BM);
-  const int64_t total = (int64_t)a.BH * n_qtiles;
-  if (total > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)total), dim3(C::THREADS), 0,
-                     (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                     (float*)a.o, a.lse, (int)a.N, n_qtiles, a.scale * kLog2e);
+static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total) {
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)total), dim3(FwdF32Cfg<D>::THREADS), 0,
+                     (hipStream_t)a.stream, p);
   return hipGetLastError();
 }
 
@@ -862,15 +1060,68 @@ int fwd_bf16_waves(int64_t BH, int64_t N, int num_cus) {
   return 2;
 }
 
+// Key splits when the query tiles alone leave compute units idle (few
+// queries per head, as in decoding, Lecture 17 page §9.2): enough splits
+// for about two workgroups per compute unit, each split at least two
+// 128-key tiles long.
+int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) {
+  const int bm = fp32 ? FwdF32Cfg<64>::BM : 32 * fwd_bf16_waves(BH, Nq, num_cus);
+  const int64_t tiles = BH * ((Nq + bm - 1) / bm);
+  if (tiles <= 0 || tiles >= num_cus) return 1;
+  const int64_t key_tiles = (Nk + kSplitAlign - 1) / kSplitAlign;
+  int64_t s = (2 * (int64_t)num_cus + tiles - 1) / tiles;
+  s = s < key_tiles / 2 ? s : key_tiles / 2;
+  if (s < 2) return 1;
+  return (int)(s < kMaxSplits ? s : kMaxSplits);
+}
+
 hipError_t launch_attn_fwd(const FwdArgs& a) {
+  int64_t total = 0;
   if (a.dtype_fp32) {
-    return a.d == 64 ? launch_f32<64>(a) : launch_f32<128>(a);
+    const FwdParams p = make_params(a, FwdF32Cfg<64>::BM, &total);
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    hipError_t e = a.d == 64 ? launch_f32<64>(a, p, total) : launch_f32<128>(a, p, total);
+    if (e != hipSuccess || p.n_splits == 1) return e;
+    return launch_attn_merge(p.o_part, p.lse_part, p.n_splits, a.BH * a.Nq, a.d, a.o, a.lse, true,
+                             a.stream);
   }
-  const int nw = a.waves ? a.waves : fwd_bf16_waves(a.BH, a.N, a.num_cus);
-  if (a.d == 64) {
-    return nw == 8 ? launch_bf16<64, 8>(a) : nw == 4 ? launch_bf16<64, 4>(a) : launch_bf16<64, 2>(a);
+  const int nw = a.waves ? a.waves : fwd_bf16_waves(a.BH, a.Nq, a.num_cus);
+  const FwdParams p = make_params(a, 32 * nw, &total);
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  hipError_t e;
+  if (a.d == 64)
+    e = nw == 8 ? launch_bf16<64, 8>(a, p, total) : nw == 4 ? launch_bf16<64, 4>(a, p, total)
+                                                           : launch_bf16<64, 2>(a, p, total);
+  else
+    e = nw == 8 ? launch_bf16<128, 8>(a, p, total) : nw == 4 ? launch_bf16<128, 4>(a, p, total)
+                                                             : launch_bf16<128, 2>(a, p, total);
+  if (e != hipSuccess || p.n_splits == 1) return e;
+  return launch_attn_merge(p.o_part, p.lse_part, p.n_splits, a.BH * a.Nq, a.d, a.o, a.lse, false,
+                           a.stream);
+}
+
+hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int n_parts, int64_t rows,
+                             int64_t d, void* o, float* lse, bool out_fp32, void* stream) {
+  const int64_t threads = rows * (d / 4);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const hipStream_t st = (hipStream_t)stream;
+  if (d == 64) {
+    if (out_fp32)
+      hipLaunchKernelGGL((attn_merge_kernel<64, true>), dim3((unsigned)blocks), dim3(256), 0, st, o_part,
+                         lse_part, n_parts, rows, o, lse);
+    else
+      hipLaunchKernelGGL((attn_merge_kernel<64, false>), dim3((unsigned)blocks), dim3(256), 0, st, o_part,
+                         lse_part, n_parts, rows, o, lse);
+  } else {
+    if (out_fp32)
+      hipLaunchKernelGGL((attn_merge_kernel<128, true>), dim3((unsigned)blocks), dim3(256), 0, st, o_part,
+                         lse_part, n_parts, rows, o, lse);
+    else
+      hipLaunchKernelGGL((attn_merge_kernel<128, false>), dim3((unsigned)blocks), dim3(256), 0, st, o_part,
+                         lse_part, n_parts, rows, o, lse);
   }
-  return nw == 8 ? launch_bf16<128, 8>(a) : nw == 4 ? launch_bf16<128, 4>(a) : launch_bf16<128, 2>(a);
+  return hipGetLastError();
 }
 
 }  // namespace tattn

@@ -13,14 +13,52 @@ struct FwdArgs {
   void* o;
   float* lse;
   int64_t BH;       // batch * heads
-  int64_t N;        // sequence length (queries = keys)
+  int64_t Nq;       // queries per head
+  int64_t Nk;       // keys (and values) per head
   int64_t d;        // head dimension
   float scale;
   bool dtype_fp32;  // false: bf16
+  bool causal;      // query i sees key j iff j <= i + Nk - Nq
+  int n_splits;     // key-range splits (1: one pass; > 1: partials in `partial`, then a merge)
+  float* partial;   // workspace for n_splits > 1: O parts [S, BH, Nq, d] then LSE parts [S, BH, Nq]
   void* stream;
   int num_cus;      // compute units of the device (grid sizing)
   int waves;        // 0 = choose; else waves per workgroup of the bf16 kernel (2, 4 or 8)
 };
+
+// Parameters of one forward kernel launch (kernel argument, by value).
+// Workgroup w covers query tile qt of head bh and keys
+// [split * split_keys, min(Nk, (split + 1) * split_keys)); with n_splits == 1
+// it writes O (input dtype) and LSE, otherwise the fp32 partial result of its
+// key range to o_part / lse_part.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* o_part;    // [n_splits, BH, Nq, d]
+  float* lse_part;  // [n_splits, BH, Nq]
+  int Nq;
+  int Nk;
+  int BH;
+  int n_qtiles;
+  int n_splits;
+  int split_keys;   // multiple of 128
+  int total_tiles;  // BH * n_qtiles * n_splits
+  float c;          // scale * log2(e)
+  int causal;
+  int remap;        // XCD-contiguous tile order (non-causal launches)
+};
+
+constexpr int kMaxSplits = 128;  // largest number of key splits of one forward launch
+
+// Keys per split chosen for (Nk, n_splits): a multiple of 128.
+int64_t split_keys_for(int64_t Nk, int n_splits);
+// Number of key splits the library picks when the caller leaves it open.
+int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus);
+hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int n_parts, int64_t rows,
+                             int64_t d, void* o, float* lse, bool out_fp32, void* stream);
 
 struct BwdArgs {
   const void* q;

@@ -11,7 +11,10 @@ multiplied by its standard deviation (3 for the long-sequence workload, which
 spreads the scores so the running max is rescaled often); the tensors are
 then rounded to the workload dtype (round-to-nearest-even for bfloat16).
 Layout is [B, H, N, d], contiguous, d innermost. The oracle consumes the
-exact float64 values of the rounded tensors.
+exact float64 values of the rounded tensors. Workloads with N_q queries
+against N_k keys draw Q as [B, H, N_q, d] and K, V as [B, H, N_k, d] the same
+way (dO, if any, as [B, H, N_q, d]); a causal workload only differs in the
+mask the computation applies, not in its inputs.
 """
 
 from __future__ import annotations
@@ -33,6 +36,16 @@ class Workload:
     seed: int
     q_std: float = 1.0
     backward: bool = False
+    n_k: int | None = None   # keys per head (None: N, self-attention shape)
+    causal: bool = False
+
+    @property
+    def Nq(self) -> int:
+        return self.N
+
+    @property
+    def Nk(self) -> int:
+        return self.N if self.n_k is None else self.n_k
 
     @property
     def scale(self) -> float:
@@ -45,8 +58,12 @@ class Workload:
     def shape(self):
         return (self.B, self.H, self.N, self.d)
 
-    def with_size(self, B=None, H=None, N=None):
-        return dataclasses.replace(self, B=B or self.B, H=H or self.H, N=N or self.N)
+    def kv_shape(self):
+        return (self.B, self.H, self.Nk, self.d)
+
+    def with_size(self, B=None, H=None, N=None, n_k=None):
+        return dataclasses.replace(self, B=B or self.B, H=H or self.H, N=N or self.N,
+                                   n_k=n_k or self.n_k)
 
 
 WORKLOADS = [
@@ -56,7 +73,18 @@ WORKLOADS = [
     Workload("long_bf16_b1h16_n16384_d128_qstd3", 1, 16, 16384, 128, "bf16", seed=4, q_std=3.0),
     Workload("fwdbwd_bf16_b2h16_n4096_d128", 2, 16, 4096, 128, "bf16", seed=5, backward=True),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Workloads of the masked and unequal-length paths: causal attention at the
+# headline shape; one device's query shard (N_q = 2048 of a 16384-long
+# sequence split over 8 devices) against the whole key sequence, with the
+# long workload's spread of scores; and decoding (one new query per
+# sequence against an 8192-key history).
+EXTRA_WORKLOADS = [
+    Workload("causal_bf16_b2h16_n4096_d128", 2, 16, 4096, 128, "bf16", seed=6, causal=True),
+    Workload("shard_bf16_b1h16_nq2048_nk16384_d128_qstd3", 1, 16, 2048, 128, "bf16", seed=7,
+             q_std=3.0, n_k=16384),
+    Workload("decode_bf16_b8h16_nq1_nk8192_d128", 8, 16, 1, 128, "bf16", seed=8, n_k=8192),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 HEADLINE = WORKLOADS[2]
 
 
@@ -66,8 +94,8 @@ def make_inputs(w: Workload, with_grad_output: bool | None = None):
     g.manual_seed(w.seed)
     shape = w.shape()
     q = torch.randn(shape, generator=g, dtype=torch.float32)
-    k = torch.randn(shape, generator=g, dtype=torch.float32)
-    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(w.kv_shape(), generator=g, dtype=torch.float32)
+    v = torch.randn(w.kv_shape(), generator=g, dtype=torch.float32)
     out = {"q": q * w.q_std, "k": k, "v": v}
     if with_grad_output if with_grad_output is not None else w.backward:
         out["do"] = torch.randn(shape, generator=g, dtype=torch.float32)
