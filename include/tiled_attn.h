@@ -196,6 +196,28 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                      attn_dtype dtype, void* stream);
 
+/*
+ * Backward pass with N_q queries against N_k keys and an optional causal
+ * mask: the gradients of sum(O * dO) for O = attn_fwd_ex(q, k, v, mask).
+ *   q, o, dout     [B,H,Nq,d] bf16 inputs; lse [B,H,Nq] float (as returned by
+ *                  attn_fwd_ex for the same q, k, v, scale, mask; rows with no
+ *                  visible key carry LSE = -inf and get dQ = 0).
+ *   k, v           [B,H,Nk,d] bf16 inputs.
+ *   dq             [B,H,Nq,d] output; dk, dv [B,H,Nk,d] outputs (bf16, fp32
+ *                  accumulation, rounded once); no overlaps.
+ *   workspace      at least attn_bwd_workspace_bytes(B, H, Nq, d, dtype)
+ *                  bytes (one float per query row).
+ * A masked (query, key) pair has P = 0 and contributes to no gradient; with
+ * Nq = 0 the call writes dK = dV = 0, with Nk = 0 it writes dQ = 0. Tensors
+ * with zero rows may be NULL. Sources as for attn_bwd, the mask as for
+ * attn_fwd_ex. attn_bwd equals attn_bwd_ex with Nq = Nk = N, ATTN_MASK_NONE.
+ */
+attn_status attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                        int64_t Nk, int64_t d, float scale, attn_mask mask, attn_dtype dtype,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

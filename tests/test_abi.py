@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"attn_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
-                          "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd"}
+                          "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_ex"}
     lib = ctypes.CDLL(ta.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -172,3 +172,22 @@ def test_binding_raises_without_gpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ta.attn_fwd(q, q.clone(), q.clone())
+
+
+def _bwd_ex(ptrs=None, ws_bytes=None, B=1, H=2, Nq=128, Nk=256, d=64, scale=0.125, mask=0, dt=0):
+    p = [A + i * T for i in range(10)] if ptrs is None else ptrs
+    ws = B * H * Nq * 4 if ws_bytes is None else ws_bytes
+    return ta.library().attn_bwd_ex(*p, ws, B, H, Nq, Nk, d, scale, mask, dt, None)
+
+
+def test_bwd_ex_rejects():
+    assert _bwd_ex(mask=5) == 1 and "unknown mask" in _err()
+    assert _bwd_ex(dt=1) == 2 and "bf16 only" in _err()
+    assert _bwd_ex(ws_bytes=1 * 2 * 128 * 4 - 4) == 1 and "workspace too small" in _err()
+    p = [A + i * T for i in range(10)]
+    p[7] = p[1] + 128 * 64 * 2  # dk inside k (k holds 2 heads of 256 rows)
+    assert _bwd_ex(ptrs=p) == 1 and "dk overlaps input k" in _err()
+    p = [A + i * T for i in range(10)]
+    p[1] = 0  # k NULL with Nk > 0
+    assert _bwd_ex(ptrs=p) == 1 and "k is NULL" in _err()
+    assert _bwd_ex(ptrs=[0] * 10, Nq=0, Nk=0) == 0

@@ -292,3 +292,61 @@ def test_workload_decode_heads_sampled():
     torch.cuda.synchronize()
     heads = [(0, 0), (7, 15), (3, 4), (5, 11)]
     _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL, heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# backward with the mask and unequal lengths
+# ---------------------------------------------------------------------------
+
+def _check_bwd(x, dq, dk, dv, scale, causal, heads=None):
+    from oracle import attention_backward
+    q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    g = [to_f64(t) for t in (dq, dk, dv)]
+    heads = heads if heads is not None else list(np.ndindex(*q.shape[:2]))
+    for (b, h) in heads:
+        ref = attention_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal=causal)
+        for name, got, want in zip(("dQ", "dK", "dV"), g, ref):
+            _assert_o(f"{name}[{b},{h}]", got[b, h], want, BF16_TOL, BF16_REL)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (64, 64), (200, 200), (513, 513), (100, 700), (700, 100),
+                                   (300, 129), (1, 1000)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ex_small(Nq, Nk, d, causal):
+    w = _wl(1, 2, Nq, Nk, d, seed=60 + Nq + Nk + d)
+    x = _cuda(make_inputs(w, with_grad_output=True))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
+    dq, dk, dv = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=causal)
+    torch.cuda.synchronize()
+    _check_bwd(x, dq, dk, dv, w.scale, causal)
+    if causal and Nq > Nk:  # queries that see no key get dQ = 0 exactly
+        assert torch.all(dq[:, :, :Nq - Nk] == 0)
+
+
+def test_bwd_ex_empty_sides():
+    q = torch.randn(1, 2, 70, 64, device="cuda").to(torch.bfloat16)
+    kv = torch.randn(1, 2, 90, 64, device="cuda").to(torch.bfloat16)
+    none_q = q[:, :, :0].contiguous()
+    none_kv = kv[:, :, :0].contiguous()
+    # no query: dK = dV = 0
+    o0 = none_q.clone()
+    lse0 = torch.empty(1, 2, 0, device="cuda")
+    dq, dk, dv = ta.attn_bwd_ex(none_q, kv, kv.clone(), o0, o0.clone(), lse0)
+    # no key: O = 0, LSE = -inf from the forward, dQ = 0
+    o, lse = ta.attn_fwd_ex(q, none_kv, none_kv.clone())
+    dq2, dk2, dv2 = ta.attn_bwd_ex(q, none_kv, none_kv.clone(), o, q.clone(), lse)
+    torch.cuda.synchronize()
+    assert dk.shape == kv.shape and torch.all(dk == 0) and torch.all(dv == 0)
+    assert torch.all(dq2 == 0) and dk2.numel() == 0
+
+
+def test_workload_causal_fwd_bwd_heads_sampled():
+    # Causal attention at the forward + backward workload's shape.
+    w = _wl(2, 16, 4096, 4096, 128, seed=5, causal=True)
+    x = _cuda(make_inputs(w, with_grad_output=True))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
+    dq, dk, dv = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=True)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, True, BF16_TOL, BF16_REL, heads=[(0, 0), (1, 15)])
+    _check_bwd(x, dq, dk, dv, w.scale, True, heads=[(0, 0), (1, 15)])

@@ -15,7 +15,7 @@ import math
 import os
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
-           "attn_merge", "attn_bwd", "attn_bwd_workspace_bytes", "library", "AttnError",
+           "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "library", "AttnError",
            "ATTN_BF16", "ATTN_FP32", "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtiledattn.so")
@@ -67,6 +67,10 @@ def library():
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                              ctypes.c_size_t, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int, c_vp]
+    lib.attn_bwd_ex.restype = ctypes.c_int
+    lib.attn_bwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                ctypes.c_size_t, c_i64, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int,
+                                ctypes.c_int, c_vp]
     _lib = lib
     return lib
 
@@ -249,5 +253,43 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, *, dq=None, dk=None, dv=None, work
                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           B, H, N, d, float(scale), code, _stream(dev, stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def attn_bwd_ex(q, k, v, o, do, lse, scale=None, *, causal=False, dq=None, dk=None, dv=None,
+                workspace=None, stream=None):
+    """dQ, dK, dV for q, o, do [B, H, Nq, d] and k, v [B, H, Nk, d] (see attn_bwd_ex). bf16."""
+    import torch
+    lib = library()
+    _shape4("q", q)
+    dt, dev = q.dtype, q.device
+    B, H, Nq, d = q.shape
+    _shape4("k", k, None, dt, dev)
+    Nk = k.shape[2]
+    _shape4("k", k, (B, H, Nk, d), dt, dev)
+    _shape4("v", v, (B, H, Nk, d), dt, dev)
+    for name, t in (("o", o), ("do", do)):
+        _shape4(name, t, (B, H, Nq, d), dt, dev)
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _shape4("dq", dq, (B, H, Nq, d), dt, dev)
+    _shape4("dk", dk, (B, H, Nk, d), dt, dev)
+    _shape4("dv", dv, (B, H, Nk, d), dt, dev)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(B, H, Nq, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
+    with torch.cuda.device(dev):
+        st = lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d,
+                             float(scale), mask, code, _stream(dev, stream))
     _check(st)
     return dq, dk, dv

@@ -279,6 +279,68 @@ attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+attn_status bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                       int64_t d, float scale, int mask, attn_dtype dtype, void* stream) {
+  int64_t q_elems = 0, q_rows = 0, k_elems = 0, k_rows = 0;
+  attn_status s = check_shape(B, H, Nq, d, dtype, &q_elems, &q_rows);
+  if (s != ATTN_OK) return s;
+  if ((s = check_shape(B, H, Nk, d, dtype, &k_elems, &k_rows)) != ATTN_OK) return s;
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
+  if ((s = check_scale(scale)) != ATTN_OK) return s;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown mask %d", mask);
+  if (q_rows == 0 && k_rows == 0) return ok();
+  // Tensors of zero rows may be NULL; the others must be valid.
+  const struct { const void* p; const char* n; int64_t rows; } ins[] = {
+      {q, "q", q_rows}, {k, "k", k_rows}, {v, "v", k_rows}, {o, "o", q_rows},
+      {dout, "dout", q_rows}, {lse, "lse", q_rows}};
+  const struct { const void* p; const char* n; int64_t rows; } outs[] = {
+      {dq, "dq", q_rows}, {dk, "dk", k_rows}, {dv, "dv", k_rows}, {workspace, "workspace", q_rows}};
+  for (auto& x : ins)
+    if (x.rows > 0 && (s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
+  for (auto& x : outs)
+    if (x.rows > 0 && (s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
+  const size_t need = (size_t)q_rows * sizeof(float);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  Range rin[6], rout[4];
+  for (int i = 0; i < 6; ++i) {
+    const uintptr_t bytes = i == 5 ? (uintptr_t)ins[i].rows * 4 : (uintptr_t)ins[i].rows * d * 2;
+    rin[i] = {ins[i].n, (uintptr_t)ins[i].p, (uintptr_t)ins[i].p + bytes};
+  }
+  for (int i = 0; i < 4; ++i) {
+    const uintptr_t bytes = i == 3 ? need : (uintptr_t)outs[i].rows * d * 2;
+    rout[i] = {outs[i].n, (uintptr_t)outs[i].p, (uintptr_t)outs[i].p + bytes};
+  }
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(rout[i], rin[j]))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", rout[i].name, rin[j].name);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(rout[i], rout[j]))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs %s and %s overlap", rout[i].name, rout[j].name);
+  }
+  int cus = 0;
+  if ((s = device_cus(&cus)) != ATTN_OK) return s;
+  tattn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B * H, Nq, Nk, d, scale,
+                   mask == ATTN_MASK_CAUSAL, stream, cus};
+  const hipError_t e = tattn::launch_attn_bwd(a);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype dtype) {
   int64_t elems = 0, rows = 0;
   if (check_shape(B, H, N, d, dtype, &elems, &rows) != ATTN_OK) return 0;
@@ -289,46 +351,17 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
                      float scale, attn_dtype dtype, void* stream) {
-  int64_t elems = 0, rows = 0;
-  attn_status s = check_shape(B, H, N, d, dtype, &elems, &rows);
-  if (s != ATTN_OK) return s;
-  if (dtype != ATTN_BF16)
-    return fail(ATTN_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
-  if ((s = check_scale(scale)) != ATTN_OK) return s;
-  if (rows == 0) return ok();
-  const struct { const void* p; const char* n; } ins[] = {
-      {q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}};
-  const struct { const void* p; const char* n; } outs[] = {
-      {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {workspace, "workspace"}};
-  for (auto& x : ins)
-    if ((s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
-  for (auto& x : outs)
-    if ((s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
-  const size_t need = (size_t)rows * sizeof(float);
-  if (workspace_bytes < need)
-    return fail(ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
-                workspace_bytes, need);
-  const uintptr_t tb = (uintptr_t)elems * 2, lb = (uintptr_t)rows * 4;
-  Range rin[6], rout[4];
-  for (int i = 0; i < 6; ++i)
-    rin[i] = {ins[i].n, (uintptr_t)ins[i].p, (uintptr_t)ins[i].p + (i == 5 ? lb : tb)};
-  for (int i = 0; i < 4; ++i)
-    rout[i] = {outs[i].n, (uintptr_t)outs[i].p, (uintptr_t)outs[i].p + (i == 3 ? need : tb)};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(rout[i], rin[j]))
-        return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", rout[i].name, rin[j].name);
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(rout[i], rout[j]))
-        return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs %s and %s overlap", rout[i].name, rout[j].name);
-  }
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, N, d,
+                    scale, ATTN_MASK_NONE, dtype, stream);
+}
 
-  int cus = 0;
-  if ((s = device_cus(&cus)) != ATTN_OK) return s;
-  tattn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B * H, N, d, scale, stream, cus};
-  const hipError_t e = tattn::launch_attn_bwd(a);
-  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
-  return ok();
+attn_status attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                        int64_t Nk, int64_t d, float scale, attn_mask mask, attn_dtype dtype,
+                        void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                    scale, (int)mask, dtype, stream);
 }
 
 }  // extern "C"

@@ -23,6 +23,8 @@
 //                dQ^T += K^T dS^T (K^T via transposed LDS reads).
 // The recomputation of S, P and dP in both sweeps trades extra MFMA work for
 // never storing dS or taking atomics on dQ.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -71,12 +73,19 @@ struct DkdvCfg {
   static_assert(CHUNKS % THREADS == 0, "tile must split evenly");
 };
 
+// Query tiles a dK/dV workgroup needs under the causal mask (query i sees
+// key j iff j <= i + Nk - Nq): from the first query that sees the tile's
+// first key; tiles before j_full hold a (query, key) pair the mask hides.
+// A key tile's mask edge spans at most BKV - 1 + BQ - 1 query positions, so
+// at most kMaxMaskedSteps query tiles are masked (3 for 128 keys, 64 queries).
+constexpr int kMaxMaskedSteps = 3;
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int n_ktiles, int total_tiles, float c,
-    float scale, int remap) {
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int BH, int n_ktiles,
+    int total_tiles, float c, float scale, int causal, int remap) {
   using C = DkdvCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * C::TILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][C::BQ];  // [buf][lse2 | D][query]
@@ -84,13 +93,28 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
   auto qs = [&](int b) { return smem + 2 * b * C::TILE; };
   auto ds = [&](int b) { return smem + (2 * b + 1) * C::TILE; };
 
-  const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
-  const int bh = tile / n_ktiles;
-  const int kt = tile - bh * n_ktiles;
-  const size_t base = (size_t)bh * N * D;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lk = lane & 31, h = lane >> 5;
+  // Causal launches take the key tiles that see the most queries (the
+  // first ones) first; others keep one head's tiles on one XCD.
+  int bh, kt;
+  if (causal) {
+    kt = (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x - kt * BH;
+  } else {
+    const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
+    bh = tile / n_ktiles;
+    kt = tile - bh * n_ktiles;
+  }
+  bh = __builtin_amdgcn_readfirstlane(bh);
+  kt = __builtin_amdgcn_readfirstlane(kt);
+  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const int tid = threadIdx.x, lane = tid & 63, lk = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int key = kt * C::BKV + wave * 32 + lk;  // the key this lane owns
-  const bool k_ok = key < N;
+  const bool k_ok = key < Nk;
+  const int off = Nk - Nq;
+  const int k_lo = kt * C::BKV, k_hi = min(k_lo + C::BKV, Nk) - 1;
+  const int j0 = causal ? max(0, k_lo - off) / C::BQ : 0;
+  const int j_full = causal ? max(0, (k_hi - off + C::BQ - 1) / C::BQ) : 0;
 
   // K^T and V^T as B operands: lane (key lk, half h) holds d = 16 s + 8 h .. +7.
   bf16x8 kf[C::DK], vf[C::DK];
@@ -98,8 +122,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
   for (int s = 0; s < C::DK; ++s) {
     u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (k_ok) {
-      x = *(const u32x4*)(K + base + (size_t)key * D + 16 * s + 8 * h);
-      y = *(const u32x4*)(V + base + (size_t)key * D + 16 * s + 8 * h);
+      x = *(const u32x4*)(K + kbase + (size_t)key * D + 16 * s + 8 * h);
+      y = *(const u32x4*)(V + kbase + (size_t)key * D + 16 * s + 8 * h);
     }
     kf[s] = as_bf16x8(x);
     vf[s] = as_bf16x8(y);
@@ -113,9 +137,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
       const int ch = tid + i * C::THREADS;
       const int row = ch / (D / 8), col = (ch % (D / 8)) * 8, q = j * C::BQ + row;
       u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      if (q < N) {
-        a = *(const u32x4*)(Q + base + (size_t)q * D + col);
-        b = *(const u32x4*)(dO + base + (size_t)q * D + col);
+      if (q < Nq) {
+        a = *(const u32x4*)(Q + qbase + (size_t)q * D + col);
+        b = *(const u32x4*)(dO + qbase + (size_t)q * D + col);
       }
       qreg[i] = a;
       dreg[i] = b;
@@ -123,9 +147,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
     if (tid < 2 * C::BQ) {
       const int q = j * C::BQ + (tid % C::BQ);
       if (tid < C::BQ)
-        sreg = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;  // P = 0 past N
+        sreg = q < Nq ? LSE[(size_t)bh * Nq + q] * kLog2e : INFINITY;  // P = 0 past Nq
       else
-        sreg = q < N ? Dv[(size_t)bh * N + q] : 0.f;
+        sreg = q < Nq ? Dv[(size_t)bh * Nq + q] : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -149,12 +173,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
   const int tr_col = 16 * (g & 1) + 4 * (j16 & 3);
   const int tr_row = 4 * h + (j16 >> 2);  // LDS row of query 16t + 8h + e is 16t + 4h + e (e < 4)
 
-  const int n_qt = (N + C::BQ - 1) / C::BQ;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_qt; ++j) {
+  const int n_qt = (Nq + C::BQ - 1) / C::BQ;
+  auto step = [&](auto masked, int j) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = j & 1;
     if (j + 1 < n_qt) load_tile(j + 1);
 
@@ -177,8 +198,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const int qi = 16 * (i >> 3) + (i & 7);
-        const float p0 = fast_exp2(fmaf(sacc[i], c, -lse2[qi]));
-        const float p1 = fast_exp2(fmaf(sacc[i + 1], c, -lse2[qi + 1]));
+        float p0 = fast_exp2(fmaf(sacc[i], c, -lse2[qi]));
+        float p1 = fast_exp2(fmaf(sacc[i + 1], c, -lse2[qi + 1]));
+        if (MASKED) {  // hidden pairs (key > query + Nk - Nq) get P = 0
+          const int q0 = j * C::BQ + 32 * qb + 8 * h + qi;
+          p0 = key > q0 + off ? 0.f : p0;
+          p1 = key > q0 + 1 + off ? 0.f : p1;
+        }
         const float s0 = p0 * (dpacc[i] - drow[qi]);
         const float s1 = p1 * (dpacc[i + 1] - drow[qi + 1]);
         pk[qb][i >> 1] = pack_bf16x2(p0, p1);
@@ -206,11 +232,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
 
     if (j + 1 < n_qt) store_tile(cur ^ 1);
     __syncthreads();
+  };
+
+  if (j0 < n_qt) {
+    load_tile(j0);
+    store_tile(j0 & 1);
+    __syncthreads();
   }
+  int j = j0;
+#pragma unroll
+  for (int m = 0; m < kMaxMaskedSteps; ++m)
+    if (j < min(j_full, n_qt)) step(std::true_type{}, j++);
+  for (; j < n_qt; ++j) step(std::false_type{}, j);
 
   if (k_ok) {
-    bf16* dkrow = dK + base + (size_t)key * D;
-    bf16* dvrow = dV + base + (size_t)key * D;
+    bf16* dkrow = dK + kbase + (size_t)key * D;
+    bf16* dvrow = dV + kbase + (size_t)key * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -247,35 +284,57 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16* __restrict__ dQ, int N, int n_qtiles, int total_tiles, float c, float scale,
-    int remap) {
+    bf16* __restrict__ dQ, int Nq, int Nk, int BH, int n_qtiles, int total_tiles, float c,
+    float scale, int causal, int remap) {
   using C = DqCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * C::TILE];
   // stage b: K tile at smem + 2 b TILE, V tile right after it
   auto ks = [&](int b) { return smem + 2 * b * C::TILE; };
   auto vs = [&](int b) { return smem + (2 * b + 1) * C::TILE; };
 
-  const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
-  const int bh = tile / n_qtiles;
-  const int qt = tile - bh * n_qtiles;
-  const size_t base = (size_t)bh * N * D;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  // Causal launches take the query tiles that see the most keys (the last
+  // ones) first; others keep one head's tiles on one XCD.
+  int bh, qt;
+  if (causal) {
+    const int r = (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x - r * BH;
+    qt = n_qtiles - 1 - r;
+  } else {
+    const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
+    bh = tile / n_qtiles;
+    qt = tile - bh * n_qtiles;
+  }
+  bh = __builtin_amdgcn_readfirstlane(bh);
+  qt = __builtin_amdgcn_readfirstlane(qt);
+  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q_row = qt * C::BM + wave * 32 + lq;
-  const bool q_ok = q_row < N;
+  const bool q_ok = q_row < Nq;
+  // Keys this tile's queries see: up to the last query's causal window;
+  // tiles from n_full on hold a key some query of the tile may not see.
+  const int off = Nk - Nq;
+  const int q_lo = qt * C::BM, q_hi = min(q_lo + C::BM, Nq) - 1;
+  const int lim = causal ? min(Nk, q_hi + off + 1) : Nk;
+  const int n_kt = lim > 0 ? (lim + C::BN - 1) / C::BN : 0;
+  const int all_see = causal ? min(Nk, q_lo + off + 1) : Nk;
+  const int n_full = all_see > 0 ? all_see / C::BN : 0;
+  const int kmax = causal ? min(Nk - 1, q_row + off) : Nk - 1;  // last key this lane's query sees
 
   bf16x8 qf[C::DK], dof[C::DK];
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
     u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (q_ok) {
-      x = *(const u32x4*)(Q + base + (size_t)q_row * D + 16 * s + 8 * h);
-      y = *(const u32x4*)(dO + base + (size_t)q_row * D + 16 * s + 8 * h);
+      x = *(const u32x4*)(Q + qbase + (size_t)q_row * D + 16 * s + 8 * h);
+      y = *(const u32x4*)(dO + qbase + (size_t)q_row * D + 16 * s + 8 * h);
     }
     qf[s] = as_bf16x8(x);
     dof[s] = as_bf16x8(y);
   }
-  const float lse2 = q_ok ? LSE[(size_t)bh * N + q_row] * kLog2e : INFINITY;
-  const float drow = q_ok ? Dv[(size_t)bh * N + q_row] : 0.f;
+  // A query that sees no key has LSE = -inf; all its keys are masked.
+  const float lse2 = q_ok ? LSE[(size_t)bh * Nq + q_row] * kLog2e : INFINITY;
+  const float drow = q_ok ? Dv[(size_t)bh * Nq + q_row] : 0.f;
 
   u32x4 kreg[C::CPT], vreg[C::CPT];
   auto load_tile = [&](int j) {
@@ -284,9 +343,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
       const int ch = tid + i * C::THREADS;
       const int row = ch / (D / 8), col = (ch % (D / 8)) * 8, kk = j * C::BN + row;
       u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      if (kk < N) {
-        a = *(const u32x4*)(K + base + (size_t)kk * D + col);
-        b = *(const u32x4*)(V + base + (size_t)kk * D + col);
+      if (kk < Nk) {
+        a = *(const u32x4*)(K + kbase + (size_t)kk * D + col);
+        b = *(const u32x4*)(V + kbase + (size_t)kk * D + col);
       }
       kreg[i] = a;
       vreg[i] = b;
@@ -312,15 +371,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
   const int tr_col = 16 * (g & 1) + 4 * (j16 & 3);
   const int tr_row = 4 * h + (j16 >> 2);
 
-  const int n_kt = (N + C::BN - 1) / C::BN;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_kt; ++j) {
+  auto step = [&](auto masked, int j) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = j & 1;
     if (j + 1 < n_kt) load_tile(j + 1);
-    const bool ragged = (j + 1) * C::BN > N;
 
     unsigned dsk[2][8];
 #pragma unroll
@@ -340,10 +394,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
       for (int i = 0; i < 16; i += 2) {
         float p0 = fast_exp2(fmaf(sacc[i], c, -lse2));
         float p1 = fast_exp2(fmaf(sacc[i + 1], c, -lse2));
-        if (ragged) {
+        if (MASKED) {  // keys past kmax (ragged end or causal window) get P = 0
           const int k0 = j * C::BN + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7);
-          if (k0 >= N) p0 = 0.f;
-          if (k0 + 1 >= N) p1 = 0.f;
+          p0 = k0 > kmax ? 0.f : p0;
+          p1 = k0 + 1 > kmax ? 0.f : p1;
         }
         dsk[kb][i >> 1] = pack_bf16x2(p0 * (dpacc[i] - drow), p1 * (dpacc[i + 1] - drow));
       }
@@ -364,10 +418,24 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
 
     if (j + 1 < n_kt) store_tile(cur ^ 1);
     __syncthreads();
+  };
+
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
   }
+  // Key tiles from n_full on are masked: at most kMaxMaskedSteps of them
+  // (a BM-query tile's mask edge spans BM - 1 keys plus a ragged end).
+  const int n_plain = min(n_full, n_kt);
+  int j = 0;
+  for (; j < n_plain; ++j) step(std::false_type{}, j);
+#pragma unroll
+  for (int m = 0; m < kMaxMaskedSteps; ++m)
+    if (j < n_kt) step(std::true_type{}, j++);
 
   if (q_ok) {
-    bf16* row = dQ + base + (size_t)q_row * D;
+    bf16* row = dQ + qbase + (size_t)q_row * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -385,8 +453,10 @@ template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   const hipStream_t st = (hipStream_t)a.stream;
   const float c = a.scale * kLog2e;
-  const int64_t rows = a.BH * a.N;
-  {
+  // With no query, the dK/dV kernel alone runs (it writes zeros); with no
+  // key, the dQ kernel alone runs (likewise).
+  const int64_t rows = a.BH * a.Nq;
+  if (rows > 0) {
     constexpr int rows_per_block = 256 / (D / 8);
     const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -395,29 +465,32 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (a.Nk > 0) {
     constexpr int NW = 4;
-    const int n_kt = (int)((a.N + 32 * NW - 1) / (32 * NW));
+    const int n_kt = (int)((a.Nk + 32 * NW - 1) / (32 * NW));
     const int64_t total = a.BH * n_kt;
     if (total > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
-                       a.lse, a.row_dot, (bf16*)a.dk, (bf16*)a.dv, (int)a.N, n_kt, (int)total, c,
-                       a.scale, (int)(total % 8 == 0));
+                       a.lse, a.row_dot, (bf16*)a.dk, (bf16*)a.dv, (int)a.Nq, (int)a.Nk, (int)a.BH,
+                       n_kt, (int)total, c, a.scale, a.causal ? 1 : 0,
+                       (int)(!a.causal && total % 8 == 0));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (rows > 0) {
     constexpr int NW = 4;
-    const int n_qt = (int)((a.N + 32 * NW - 1) / (32 * NW));
+    const int n_qt = (int)((a.Nq + 32 * NW - 1) / (32 * NW));
     const int64_t total = a.BH * n_qt;
     if (total > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
-                       a.lse, a.row_dot, (bf16*)a.dq, (int)a.N, n_qt, (int)total, c, a.scale,
-                       (int)(total % 8 == 0));
-    return hipGetLastError();
+                       a.lse, a.row_dot, (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH, n_qt,
+                       (int)total, c, a.scale, a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 hipError_t launch_attn_bwd(const BwdArgs& a) {

@@ -70,11 +70,13 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* row_dot;   // workspace: D_i = dO_i . O_i, [BH, N] floats
+  float* row_dot;   // workspace: D_i = dO_i . O_i, [BH, Nq] floats
   int64_t BH;
-  int64_t N;
+  int64_t Nq;       // queries per head (q, o, dout, lse, dq)
+  int64_t Nk;       // keys per head (k, v, dk, dv)
   int64_t d;
   float scale;
+  bool causal;      // query i sees key j iff j <= i + Nk - Nq
   void* stream;
   int num_cus;
 };
