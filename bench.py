@@ -62,8 +62,10 @@ def cpu_baseline(w, x, seconds):
 
     q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    # whole heads, cycling over the workload's heads until the budget is spent
     done, t0 = 0, time.perf_counter()
-    for (b, h) in heads:
+    while True:
+        b, h = heads[done % len(heads)]
         attention_forward(q[b, h], k[b, h], v[b, h], w.scale)
         done += 1
         if time.perf_counter() - t0 >= seconds:
@@ -77,10 +79,78 @@ def cpu_baseline(w, x, seconds):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} of {len(heads)} heads of {w.name} (float64 NumPy, S and P materialised), "
+        "sample": f"{done} head evaluations (the workload has {len(heads)} heads) of {w.name} "
+                  f"(float64 NumPy, S and P materialised), "
                   f"{el:.1f} s; BLAS threads {threads}, host CPUs {len(os.sched_getaffinity(0))}",
         "seconds": el,
     }
+
+
+def _time_ms(fn, stream, warm, n):
+    """Average milliseconds of fn() over n calls after warm calls (HIP events on `stream`)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def measure_ex(ta, pm, dev, stream, n):
+    """Figures of the masked and unequal-length paths (not the headline metric).
+
+    causal: forward and backward at the headline shape, TFLOP/s over the
+    visible (query, key) pairs (4 d resp. 10 d FLOPs per pair); shard: one
+    device's 2048 queries of a 16384-long sequence against all its keys
+    (library-chosen key splits); decode: one query per sequence against 8192
+    keys, bound by reading K and V (GB/s against 8 TB/s).
+    """
+    import torch
+
+    from tiled_attention_17_amd.workloads import EXTRA_WORKLOADS, make_inputs
+
+    out = {}
+    peak = pm.MI355X_PEAK_FLOPS["bf16"] / 1e12
+    for w in EXTRA_WORKLOADS:
+        x = {k: t.to(dev) for k, t in make_inputs(w, with_grad_output=w.causal).items()}
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        splits = 1 if w.causal else ta.attn_fwd_ex_auto_splits(w.B, w.H, w.Nq, w.Nk, w.d)
+        need = ta.attn_fwd_ex_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, splits)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=w.causal, num_splits=splits,
+                           out=o, lse=lse, workspace=ws)
+
+        ms = _time_ms(fwd, stream, 3 * n, n)
+        fl = pm.attn_fwd_flops_masked(w.B, w.H, w.Nq, w.Nk, w.d, w.causal)
+        nbytes = pm.attn_fwd_bytes_ex(w.B, w.H, w.Nq, w.Nk, w.d, 2)
+        r = {"workload": w.name, "splits": splits, "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+             "pct_of_bf16_dense_peak": 100.0 * fl / (ms * 1e-3) / 1e12 / peak,
+             "gb_per_s": nbytes / (ms * 1e-3) / 1e9,
+             "pct_of_hbm": 100.0 * nbytes / (ms * 1e-3) / pm.MI355X_HBM_BYTES_PER_S}
+        if w.causal:
+            g = [torch.empty_like(x["q"]) for _ in range(3)]
+            bws = torch.empty(ta.attn_bwd_workspace_bytes(w.B, w.H, w.Nq, w.d), dtype=torch.uint8,
+                              device=dev)
+
+            def bwd():
+                ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=True,
+                               dq=g[0], dk=g[1], dv=g[2], workspace=bws)
+
+            bms = _time_ms(bwd, stream, 3, max(3, n // 5))
+            bfl = pm.attn_bwd_flops_masked(w.B, w.H, w.Nq, w.Nk, w.d, True)
+            r.update({"bwd_ms": bms, "bwd_tflops": bfl / (bms * 1e-3) / 1e12})
+            del g, bws
+        out[w.name.split("_")[0]] = r
+        del x, o, lse, ws
+    return out
 
 
 def main():
@@ -95,6 +165,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward figures in 'extra'")
+    ap.add_argument("--no-ex", action="store_true",
+                    help="skip the causal / unequal-length / decoding figures in 'extra'")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -180,6 +252,9 @@ def main():
             / ((ms_per_step + bms) * 1e-3) / 1e12,
         })
         del xb, ob, lb, g, ws
+
+    if not args.no_ex:
+        extra.update(measure_ex(ta, pm, dev, stream, max(20, K // 4)))
 
     traffic = measured_traffic()
     result = {

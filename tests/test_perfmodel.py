@@ -57,3 +57,22 @@ def test_attention_counts(B, H, N, d, e, flops, nbytes):
     # each forward FLOP count is two matmuls per head
     assert pm.attn_fwd_flops(B, H, N, d) == B * H * (pm.matmul_flops(N, d, N) + pm.matmul_flops(N, N, d))
     assert pm.attn_bwd_flops(B, H, N, d) == B * H * 5 * pm.matmul_flops(N, d, N)
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 1), (5, 5), (4096, 4096), (3, 7), (7, 3), (1, 9), (9, 1),
+                                   (100, 37), (37, 100)])
+def test_visible_pairs_counts_the_causal_mask(nq, nk):
+    brute = sum(1 for i in range(min(nq, 300)) for j in range(nk) if j <= i + nk - nq) \
+        if nq <= 300 else None
+    got = pm.visible_pairs(nq, nk, True)
+    if brute is not None:
+        assert got == brute
+    else:
+        assert got == nq * (nq + 1) // 2  # equal lengths: the lower triangle with its diagonal
+    assert pm.visible_pairs(nq, nk, False) == nq * nk
+    assert pm.attn_fwd_flops_masked(2, 3, nq, nk, 64, True) == 4 * 6 * 64 * got
+    assert pm.attn_bwd_flops_masked(2, 3, nq, nk, 64, False) == 10 * 6 * 64 * nq * nk
+
+
+def test_fwd_bytes_ex_reduces_to_self_attention():
+    assert pm.attn_fwd_bytes_ex(2, 16, 4096, 4096, 128, 2) == pm.attn_fwd_bytes(2, 16, 4096, 128, 2)

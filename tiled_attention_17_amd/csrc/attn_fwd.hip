@@ -1049,30 +1049,42 @@ static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total
   return hipGetLastError();
 }
 
-// Workgroup size choice: the largest query tile whose grid still covers
-// every compute unit at least once (wave quantization, CS336 Lecture 5
-// notes §6.2), else the smallest.
-int fwd_bf16_waves(int64_t BH, int64_t N, int num_cus) {
+// Workgroup size choice: the largest query tile whose grid (with the key
+// splits) still covers every compute unit at least once (wave quantization,
+// CS336 Lecture 5 notes §6.2), else the smallest; tiles of more than twice
+// the query count (mostly empty rows, as in decoding) are passed over.
+int fwd_bf16_waves(int64_t BH, int64_t Nq, int64_t splits, int num_cus) {
   for (int nw : {8, 4}) {
-    const int64_t tiles = BH * ((N + 32 * nw - 1) / (32 * nw));
+    if (32 * nw > 2 * Nq) continue;
+    const int64_t tiles = BH * ((Nq + 32 * nw - 1) / (32 * nw)) * splits;
     if (tiles >= num_cus) return nw;
   }
   return 2;
 }
 
 // Key splits when the query tiles alone leave compute units idle (few
-// queries per head, as in decoding, Lecture 17 page §9.2): enough splits
-// for about two workgroups per compute unit, each split at least two
-// 128-key tiles long.
+// query tiles per head, as for one device's query shard or in decoding,
+// Lecture 17 page §9.2). With at least 128 queries the 256-query ping-pong
+// tiles are split until they fill the chip once (each split keeping at least
+// four 128-key tiles); with fewer, the smaller tiles are split for about two
+// workgroups per compute unit (each split at least two 128-key tiles).
 int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) {
-  const int bm = fp32 ? FwdF32Cfg<64>::BM : 32 * fwd_bf16_waves(BH, Nq, num_cus);
+  const int64_t key_tiles = (Nk + kSplitAlign - 1) / kSplitAlign;
+  auto clamp_splits = [&](int64_t s, int64_t min_tiles) -> int {
+    s = s < key_tiles / min_tiles ? s : key_tiles / min_tiles;
+    if (s < 2) return 1;
+    return (int)(s < kMaxSplits ? s : kMaxSplits);
+  };
+  if (!fp32 && Nq >= 128) {
+    const int64_t t8 = BH * ((Nq + 255) / 256);
+    if (t8 >= num_cus) return 1;
+    const int s = clamp_splits((num_cus + t8 - 1) / t8, 4);
+    if (s > 1) return s;
+  }
+  const int bm = fp32 ? FwdF32Cfg<64>::BM : 32 * fwd_bf16_waves(BH, Nq, 1, num_cus);
   const int64_t tiles = BH * ((Nq + bm - 1) / bm);
   if (tiles <= 0 || tiles >= num_cus) return 1;
-  const int64_t key_tiles = (Nk + kSplitAlign - 1) / kSplitAlign;
-  int64_t s = (2 * (int64_t)num_cus + tiles - 1) / tiles;
-  s = s < key_tiles / 2 ? s : key_tiles / 2;
-  if (s < 2) return 1;
-  return (int)(s < kMaxSplits ? s : kMaxSplits);
+  return clamp_splits((2 * (int64_t)num_cus + tiles - 1) / tiles, 2);
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a) {
@@ -1085,7 +1097,10 @@ hipError_t launch_attn_fwd(const FwdArgs& a) {
     return launch_attn_merge(p.o_part, p.lse_part, p.n_splits, a.BH * a.Nq, a.d, a.o, a.lse, true,
                              a.stream);
   }
-  const int nw = a.waves ? a.waves : fwd_bf16_waves(a.BH, a.Nq, a.num_cus);
+  const int64_t splits = a.n_splits > 1 ? (a.Nk + split_keys_for(a.Nk, a.n_splits) - 1) /
+                                               split_keys_for(a.Nk, a.n_splits)
+                                         : 1;
+  const int nw = a.waves ? a.waves : fwd_bf16_waves(a.BH, a.Nq, splits, a.num_cus);
   const FwdParams p = make_params(a, 32 * nw, &total);
   if (total > INT32_MAX) return hipErrorInvalidValue;
   hipError_t e;

@@ -83,6 +83,6 @@ struct BwdArgs {
 
 hipError_t launch_attn_fwd(const FwdArgs& a);
 hipError_t launch_attn_bwd(const BwdArgs& a);
-int fwd_bf16_waves(int64_t BH, int64_t N, int num_cus);
+int fwd_bf16_waves(int64_t BH, int64_t Nq, int64_t splits, int num_cus);
 
 }  // namespace tattn

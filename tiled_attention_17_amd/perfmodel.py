@@ -75,3 +75,31 @@ def attn_fwd_bytes(B, H, N, d, elem_bytes):
 def attn_bwd_bytes(B, H, N, d, elem_bytes):
     """Read Q, K, V, O, dO and write dQ, dK, dV once; LSE read, row term D written and read (fp32)."""
     return B * H * (8 * N * d * elem_bytes + 3 * N * 4)
+
+
+def visible_pairs(Nq, Nk, causal):
+    """(query, key) pairs the attention covers: all Nq * Nk, or under the causal
+    mask (query i sees key j iff j <= i + Nk - Nq) sum_i clamp(i + Nk - Nq + 1, 0, Nk)."""
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq
+    # rows i < -off see nothing; rows from Nq - 1 - ... see all Nk keys once i + off + 1 >= Nk
+    lo = max(0, -off)                  # first row with a visible key
+    full = max(lo, min(Nq, Nk - off - 1))  # first row that sees every key
+    ramp = sum(range(lo + off + 1, full + off + 1)) if full > lo else 0
+    return ramp + (Nq - full) * Nk
+
+
+def attn_fwd_flops_masked(B, H, Nq, Nk, d, causal):
+    """Two matmuls over the visible (query, key) pairs: 4 d FLOPs per pair."""
+    return 4 * B * H * d * visible_pairs(Nq, Nk, causal)
+
+
+def attn_bwd_flops_masked(B, H, Nq, Nk, d, causal):
+    """Five matmuls over the visible pairs: 10 d FLOPs per pair."""
+    return 10 * B * H * d * visible_pairs(Nq, Nk, causal)
+
+
+def attn_fwd_bytes_ex(B, H, Nq, Nk, d, elem_bytes):
+    """Read Q and K, V once, write O once, write the fp32 LSE once."""
+    return B * H * (2 * Nq * d * elem_bytes + 2 * Nk * d * elem_bytes + 4 * Nq)
