@@ -7,6 +7,7 @@ and the oracle never imports the product library (they share no code).
 
 Sources (cited by page title and section; no line numbers):
   [L17]  "第17讲 Tensor Core、HBM、SRAM 与 FlashAttention" (zwxr.cn news 250415),
+         §2.1 (the matrix product), §5.3 (its work count),
          §8.1 (scaled dot-product attention), §8.3 (online softmax state
          m, l, o and its update rule; masks and causal attention named as
          part of a real kernel), §8.4 (exact, not bitwise identical),
@@ -32,3 +33,4 @@ from .attention import (  # noqa: F401
     causal_visible,
     merge_partials,
 )
+from .matmul import brute_force_matmul_nt, matmul_nt  # noqa: F401
