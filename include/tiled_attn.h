@@ -168,6 +168,20 @@ attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num
                        int64_t H, int64_t N, int64_t d, void* o, float* lse, attn_dtype dtype,
                        void* stream);
 
+/*
+ * Matrix product C = A B^T (the tiled GEMM of the Lecture 17 page §2.1 and
+ * §5.2-§5.3; B given as [N, K], both operands contiguous along k).
+ *   a  [M, K] bf16, b [N, K] bf16, c [M, N] bf16 output (fp32 accumulation,
+ *      rounded once, RNE); dense row-major, 16-byte aligned; c must not
+ *      overlap a or b. M*K*2 and N*K*2 < 2^31; K a multiple of 8.
+ * One workgroup computes one 128 x 128 tile of C, so the work comes in
+ * ceil(M/128) * ceil(N/128) tiles: the unit whose count against the compute
+ * units sets wave quantization (CS336 Lecture 5 notes §6.2). K = 0 gives
+ * C = 0; M*N = 0 does nothing. bf16 only (ATTN_FP32: ATTN_ERR_UNSUPPORTED).
+ */
+attn_status attn_matmul_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
+                           attn_dtype dtype, void* stream);
+
 /* Bytes of device workspace attn_bwd needs for these sizes (the per-row
  * term D_i = sum_k dO_ik O_ik, one float per query row). */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype dtype);

@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"attn_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
-                          "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_ex"}
+                          "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_ex",
+                          "attn_matmul_nt"}
     lib = ctypes.CDLL(ta.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -191,3 +192,15 @@ def test_bwd_ex_rejects():
     p[1] = 0  # k NULL with Nk > 0
     assert _bwd_ex(ptrs=p) == 1 and "k is NULL" in _err()
     assert _bwd_ex(ptrs=[0] * 10, Nq=0, Nk=0) == 0
+
+
+def test_matmul_rejects():
+    mm = ta.library().attn_matmul_nt
+    assert mm(A, A + T, A + 2 * T, 64, 64, 64, 1, None) == 2 and "bf16 only" in _err()
+    assert mm(A, A + T, A + 2 * T, 64, 64, 60, 0, None) == 2 and "multiple of 8" in _err()
+    assert mm(A, A + T, A + 2 * T, -1, 64, 64, 0, None) == 1 and "negative" in _err()
+    assert mm(A, A + T, A + 2 * T, 1 << 20, 64, 1 << 12, 0, None) == 2 and "too large" in _err()
+    assert mm(A, A + T, A + 64, 64, 64, 64, 0, None) == 1 and "overlaps input a" in _err()
+    assert mm(A, 0, A + 2 * T, 64, 64, 64, 0, None) == 1 and "b is NULL" in _err()
+    assert mm(A + 8, A + T, A + 2 * T, 64, 64, 64, 0, None) == 1 and "aligned" in _err()
+    assert mm(0, 0, 0, 0, 64, 64, 0, None) == 0

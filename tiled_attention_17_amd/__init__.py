@@ -15,7 +15,8 @@ import math
 import os
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
-           "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "library", "AttnError",
+           "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_matmul_nt",
+           "library", "AttnError",
            "ATTN_BF16", "ATTN_FP32", "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtiledattn.so")
@@ -67,6 +68,8 @@ def library():
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                              ctypes.c_size_t, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int, c_vp]
+    lib.attn_matmul_nt.restype = ctypes.c_int
+    lib.attn_matmul_nt.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_vp]
     lib.attn_bwd_ex.restype = ctypes.c_int
     lib.attn_bwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                 ctypes.c_size_t, c_i64, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int,
@@ -293,3 +296,28 @@ def attn_bwd_ex(q, k, v, o, do, lse, scale=None, *, causal=False, dq=None, dk=No
                              float(scale), mask, code, _stream(dev, stream))
     _check(st)
     return dq, dk, dv
+
+
+def attn_matmul_nt(a, b, *, out=None, stream=None):
+    """C = A B^T for bf16 a [M, K] and b [N, K] (see attn_matmul_nt in tiled_attn.h)."""
+    import torch
+    lib = library()
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"expected a [M, K] and b [N, K], got {tuple(a.shape)} and {tuple(b.shape)}")
+    if a.dtype != b.dtype or a.device != b.device:
+        raise ValueError("a and b must share dtype and device")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    if a.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    if tuple(out.shape) != (M, N) or out.dtype != a.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor of the operands' dtype")
+    with torch.cuda.device(a.device):
+        st = lib.attn_matmul_nt(_ptr(a), _ptr(b), _ptr(out), M, N, K, _dtype_code(a),
+                                _stream(a.device, stream))
+    _check(st)
+    return out

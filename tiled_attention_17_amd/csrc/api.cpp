@@ -250,6 +250,36 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                     workspace_bytes, dtype, stream);
 }
 
+attn_status attn_matmul_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
+                           attn_dtype dtype, void* stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the matrix product is implemented for bf16 only");
+  if (M < 0 || N < 0 || K < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 8 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "K=%lld must be a multiple of 8 (16-byte rows)", (long long)K);
+  // Each operand is addressed with 32-bit byte offsets.
+  if ((M && K && M > (INT32_MAX / 2) / K) || (N && K && N > (INT32_MAX / 2) / K))
+    return fail(ATTN_ERR_UNSUPPORTED, "operand too large (M*K*2 and N*K*2 must be < 2^31)");
+  if (M > INT32_MAX || N > INT32_MAX || (M && N && M > INT64_MAX / 2 / N))
+    return fail(ATTN_ERR_UNSUPPORTED, "result too large");
+  if (M == 0 || N == 0) return ok();
+  attn_status s;
+  if ((s = check_ptr(c, "c", 16)) != ATTN_OK) return s;
+  if (K > 0 && ((s = check_ptr(a, "a", 16)) != ATTN_OK || (s = check_ptr(b, "b", 16)) != ATTN_OK))
+    return s;
+  const Range in[2] = {{"a", (uintptr_t)a, (uintptr_t)a + (uintptr_t)(M * K) * 2},
+                       {"b", (uintptr_t)b, (uintptr_t)b + (uintptr_t)(N * K) * 2}};
+  const Range out = {"c", (uintptr_t)c, (uintptr_t)c + (uintptr_t)(M * N) * 2};
+  for (const Range& x : in)
+    if (overlaps(out, x)) return fail(ATTN_ERR_INVALID_ARGUMENT, "output c overlaps input %s", x.name);
+  const hipError_t he = tattn::launch_matmul_nt(a, b, c, M, N, K, stream);
+  if (he != hipSuccess) return fail(ATTN_ERR_HIP, "matmul launch failed: %s", hipGetErrorString(he));
+  return ok();
+}
+
 attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t B,
                        int64_t H, int64_t N, int64_t d, void* o, float* lse, attn_dtype dtype,
                        void* stream) {

@@ -543,13 +543,6 @@ struct Stager {
 // the per-lane offset (the scalar offset stays 0), and staging a tile costs
 // no VALU work. Completion is waited for with vmcnt before the barrier that
 // publishes the tile.
-// One buffer_load_dwordx4 ... lds: 16 bytes per lane from byte offset
-// voff of the buffer to LDS address lds + 16 * lane. (A plain device
-// function: the host pass of a kernel template must not see the builtin.)
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
-                                           0, 0, 0);
-}
 
 template <int D, int ROWS, int WAVES = 4>
 struct KDirect {
@@ -580,9 +573,6 @@ struct KDirect {
   }
 };
 
-// Waits until this wave's vector-memory operations are done (among them the
-// buffer_load ... lds writes of a directly staged K tile).
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);

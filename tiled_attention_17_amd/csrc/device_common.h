@@ -75,6 +75,19 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 // the range check against num_records enabled.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// One buffer_load_dwordx4 ... lds: 16 bytes per lane from byte offset voff
+// of the buffer to LDS address lds + 16 * lane (the LDS side is written
+// lane-linearly; completion is counted by vmcnt). A plain device function:
+// the host pass of a kernel template must not see the builtin.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           0, 0, 0);
+}
+
+// Waits until this wave's vector-memory operations are done (among them the
+// buffer_load ... lds writes of a directly staged tile).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // 8 bf16 from two transposed 4-element LDS reads (see the header comment).
 __device__ __forceinline__ bf16x8 lds_read_tr_pair(const bf16* p0, const bf16* p1) {
   i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));

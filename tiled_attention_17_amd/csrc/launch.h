@@ -82,6 +82,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_attn_fwd(const FwdArgs& a);
+// C = A B^T, bf16: A [M, K], B [N, K], C [M, N].
+hipError_t launch_matmul_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
+                            void* stream);
 hipError_t launch_attn_bwd(const BwdArgs& a);
 int fwd_bf16_waves(int64_t BH, int64_t Nq, int64_t splits, int num_cus);
 
