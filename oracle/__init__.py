@@ -34,3 +34,12 @@ from .attention import (  # noqa: F401
     merge_partials,
 )
 from .matmul import brute_force_matmul_nt, matmul_nt  # noqa: F401
+from .fp8 import (  # noqa: F401
+    attention_forward_mxfp8,
+    e4m3_decode,
+    e4m3_encode,
+    mx_dequantize,
+    mx_quantize,
+    mx_scale_code,
+    p_rounding_bound,
+)
