@@ -108,7 +108,8 @@ def measure_ex(ta, pm, dev, stream, n):
     visible (query, key) pairs (4 d resp. 10 d FLOPs per pair); shard: one
     device's 2048 queries of a 16384-long sequence against all its keys
     (library-chosen key splits); decode: one query per sequence against 8192
-    keys, bound by reading K and V (GB/s against 8 TB/s).
+    keys, bound by reading K and V (GB/s against 8 TB/s); mxfp8: the MXFP8
+    forward at the headline shape against the fp8 dense peak.
     """
     import torch
 
@@ -150,6 +151,25 @@ def measure_ex(ta, pm, dev, stream, n):
             del g, bws
         out[w.name.split("_")[0]] = r
         del x, o, lse, ws
+
+    # MXFP8 forward at the headline shape: inputs quantized beforehand and
+    # resident as MXFP8 (the quantizer's own time reported separately)
+    from tiled_attention_17_amd.workloads import HEADLINE
+    w = HEADLINE
+    x = {k: t.to(dev) for k, t in make_inputs(w).items()}
+    q8, qs = ta.attn_quantize_mxfp8(x["q"])
+    k8, ks = ta.attn_quantize_mxfp8(x["k"])
+    vt8, vts = ta.attn_quantize_mxfp8(x["v"], transpose=True)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ms = _time_ms(lambda: ta.attn_fwd_mxfp8(q8, qs, k8, ks, vt8, vts, w.scale, out=o, lse=lse), stream,
+                  3 * n, n)
+    qms = _time_ms(lambda: (ta.attn_quantize_mxfp8(x["q"]), ta.attn_quantize_mxfp8(x["k"]),
+                            ta.attn_quantize_mxfp8(x["v"], transpose=True)), stream, 3, n)
+    fl = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
+    out["mxfp8"] = {"workload": w.name + " (MXFP8 Q, K, V^T)", "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+                    "pct_of_fp8_dense_peak": 100.0 * fl / (ms * 1e-3) / pm.MI355X_PEAK_FLOPS["fp8"],
+                    "quantize_q_k_vt_ms": qms}
     return out
 
 

@@ -182,6 +182,44 @@ attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num
 attn_status attn_matmul_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
                            attn_dtype dtype, void* stream);
 
+/*
+ * MXFP8 quantization (CS336 Lecture 5 transcript, low-precision formats:
+ * E4M3 elements, 4 exponent and 3 mantissa bits, with one power-of-two scale
+ * stored in 8 bits for every 32 consecutive elements).
+ *   x       [batch, rows, cols] bf16 input, 16-byte aligned.
+ *   transpose = 0: q [batch, rows, cols] E4M3 bytes, scales [batch, rows,
+ *           cols/32]: blocks of 32 along cols (cols % 32 == 0). This is the
+ *           layout of Q and K (blocks along d).
+ *   transpose = 1: q [batch, cols, rows], the transpose, and scales
+ *           [batch, cols, rows/32]: blocks of 32 along the original rows
+ *           (rows % 32 == 0). This is the copy V^T [d, N] that O = P V needs
+ *           (its reduction runs over the keys).
+ * Element codes: OCP E4M3 (bias 7, largest finite 448, no infinities), round
+ * to nearest even. A block's scale byte is e + 127 for the smallest e with
+ * max|x| <= 448 * 2^e (clamped to 0..254, 0 for an all-zero block), so no
+ * element saturates. q is 16-byte aligned; outputs must not overlap x.
+ * bf16 input only; finite inputs only.
+ */
+attn_status attn_quantize_mxfp8(const void* x, int64_t batch, int64_t rows, int64_t cols, int transpose,
+                                void* q, void* scales, attn_dtype dtype, void* stream);
+
+/*
+ * MXFP8 attention forward: O and LSE of softmax attention on the MXFP8
+ * inputs (attn_quantize_mxfp8 layouts), computed with gfx950's MX-scaled
+ * matrix instructions; P is rounded to MXFP8 in blocks of 32 keys before
+ * O = P V (the softmax statistics stay fp32).
+ *   q8, k8       [B,H,N,d] E4M3, 16-byte aligned; q_scales, k_scales
+ *                [B,H,N,d/32], 4-byte aligned.
+ *   vt8          [B,H,d,N] E4M3 (V transposed), 16-byte aligned; vt_scales
+ *                [B,H,d,N/32], 4-byte aligned.
+ *   o            [B,H,N,d] bf16 output; lse [B,H,N] float output (as attn_fwd).
+ * N a multiple of 32; d in {64, 128}. Error bound against attention on the
+ * dequantized inputs: |O - O_ref| <= 2^-4 (P |V|) + rounding of O to bf16.
+ */
+attn_status attn_fwd_mxfp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales,
+                           const void* vt8, const void* vt_scales, void* o, float* lse, int64_t B,
+                           int64_t H, int64_t N, int64_t d, float scale, void* stream);
+
 /* Bytes of device workspace attn_bwd needs for these sizes (the per-row
  * term D_i = sum_k dO_ik O_ik, one float per query row). */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype dtype);

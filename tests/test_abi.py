@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"attn_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
                           "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_ex",
-                          "attn_matmul_nt"}
+                          "attn_matmul_nt", "attn_quantize_mxfp8", "attn_fwd_mxfp8"}
     lib = ctypes.CDLL(ta.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -204,3 +204,25 @@ def test_matmul_rejects():
     assert mm(A, 0, A + 2 * T, 64, 64, 64, 0, None) == 1 and "b is NULL" in _err()
     assert mm(A + 8, A + T, A + 2 * T, 64, 64, 64, 0, None) == 1 and "aligned" in _err()
     assert mm(0, 0, 0, 0, 64, 64, 0, None) == 0
+
+
+def test_mxfp8_rejects():
+    lib = ta.library()
+    qz = lib.attn_quantize_mxfp8
+    assert qz(A, 2, 64, 48, 0, A + T, A + 2 * T, 0, None) == 2 and "multiple of 32" in _err()
+    assert qz(A, 2, 48, 64, 1, A + T, A + 2 * T, 0, None) == 2 and "multiple of 32" in _err()
+    assert qz(A, 2, 64, 64, 2, A + T, A + 2 * T, 0, None) == 1 and "transpose" in _err()
+    assert qz(A, 2, 64, 64, 0, A + T, A + 2 * T, 1, None) == 2 and "bf16" in _err()
+    assert qz(A, 2, 64, 64, 0, A + 64, A + 2 * T, 0, None) == 1 and "overlaps input x" in _err()
+    assert qz(0, 0, 64, 64, 0, 0, 0, 0, None) == 0
+    fw = lib.attn_fwd_mxfp8
+    p = [A + i * T for i in range(8)]
+    assert fw(*p, 1, 2, 96 + 16, 128, 0.1, None) == 2 and "multiple of 32" in _err()
+    assert fw(*p, 1, 2, 128, 96, 0.1, None) == 2
+    p2 = list(p)
+    p2[6] = p2[4] + 64  # o inside vt8
+    assert fw(*p2, 1, 2, 128, 128, 0.1, None) == 1 and "overlaps input vt8" in _err()
+    p3 = list(p)
+    p3[1] = p3[1] + 2  # q_scales not 4-byte aligned
+    assert fw(*p3, 1, 2, 128, 128, 0.1, None) == 1 and "aligned" in _err()
+    assert fw(*p, 0, 2, 128, 128, 0.1, None) == 0

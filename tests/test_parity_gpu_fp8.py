@@ -1,0 +1,151 @@
+"""GPU parity of the MXFP8 path: the quantizer bit for bit, the forward within its derived bar.
+
+Quantizer: attn_quantize_mxfp8 must reproduce the oracle's mx_quantize
+exactly (codes and scale bytes), for row blocks (Q, K) and for the
+transposed column blocks (V^T).
+
+Forward: the inputs are quantized on the CPU by the oracle (so no expected
+value comes from the GPU path), the GPU runs attn_fwd_mxfp8 on those codes,
+and the oracle computes attention on the dequantized inputs. The kernel also
+rounds P to E4M3 (relative error <= 2^-4 per element) before O = P V, and O
+to bf16 (<= 2^-9 relative), so every element must satisfy
+  |O - O_ref| <= 2^-4 (P |V_hat|) + 2^-8 |O_ref| + 2^-12 max|V_hat| + 1e-4,
+(the third term covers probabilities far below their block's maximum, which
+E4M3 holds as subnormals); LSE uses the unrounded probabilities and keeps
+the bf16 bar of 1e-3.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import tiled_attention_17_amd as ta  # noqa: E402
+from oracle import attention_forward_mxfp8, mx_dequantize, mx_quantize, p_rounding_bound  # noqa: E402
+from tiled_attention_17_amd.workloads import Workload, make_inputs, to_f64  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ta.library()
+
+
+def _bf16(shape, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------
+# quantizer: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("std", [1.0, 1e-3, 500.0])
+@pytest.mark.parametrize("shape", [(1, 32, 32), (3, 64, 128), (2, 96, 64), (1, 160, 288)])
+def test_quantize_rows_and_columns_bit_exact(shape, std):
+    x = _bf16(shape, seed=shape[1] + shape[2], std=std)
+    x[0, 0, :32] = 0.0                       # an all-zero block
+    x[0, 1, :] = x[0, 1, :] * 2.0 ** 20      # a row far larger than the rest
+    xg = x.cuda()
+    q, s = ta.attn_quantize_mxfp8(xg)
+    qt, st = ta.attn_quantize_mxfp8(xg, transpose=True)
+    torch.cuda.synchronize()
+    xf = x.double().numpy()
+    rq, rs = mx_quantize(xf, axis=-1)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    rqt, rst = mx_quantize(np.swapaxes(xf, -1, -2), axis=-1)  # blocks along the original rows
+    np.testing.assert_array_equal(qt.cpu().numpy(), rqt)
+    np.testing.assert_array_equal(st.cpu().numpy(), rst)
+
+
+def test_quantize_empty_is_noop():
+    q, s = ta.attn_quantize_mxfp8(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    assert q.shape == (0, 64) and s.shape == (0, 2)
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def _mx_inputs(B, H, N, d, seed, q_std=1.0):
+    w = Workload(f"fp8_{B}_{H}_{N}_{d}", B, H, N, d, "bf16", seed=seed, q_std=q_std)
+    x = make_inputs(w)
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    q8, qs = mx_quantize(q)
+    k8, ks = mx_quantize(k)
+    vt8, vts = mx_quantize(np.swapaxes(v, -1, -2))  # V^T [d, N], blocks along the keys
+    return w, (q8, qs, k8, ks, vt8, vts)
+
+
+def _run(codes, scale):
+    t = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in codes]
+    o, lse = ta.attn_fwd_mxfp8(*t, scale)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+def _check(codes, o, lse, scale, heads=None):
+    q8, qs, k8, ks, vt8, vts = codes
+    B, H = q8.shape[:2]
+    heads = heads if heads is not None else list(np.ndindex(B, H))
+    for (b, h) in heads:
+        one = [a[b, h] for a in codes]
+        ro, rl = attention_forward_mxfp8(*one, scale)
+        qh, kh = mx_dequantize(one[0], one[1]), mx_dequantize(one[2], one[3])
+        vh = np.swapaxes(mx_dequantize(one[4], one[5]), -1, -2)
+        bound = p_rounding_bound(qh, kh, vh, scale) + 2.0 ** -8 * np.abs(ro) + 2.0 ** -12 * np.abs(vh).max() + 1e-4
+        err = np.abs(o[b, h] - ro)
+        assert np.all(np.isfinite(o[b, h]))
+        bad = err > bound
+        assert not bad.any(), (f"O[{b},{h}]: {bad.sum()} elements outside the bar; "
+                               f"max err {err.max():.3e}, max err/bound {(err / bound).max():.2f}")
+        lerr = np.abs(lse[b, h] - rl).max()
+        assert lerr <= LSE_TOL, f"LSE[{b},{h}]: {lerr:.3e}"
+        # the rounding of P is really there, and small against the bar
+        assert err.max() > 0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [32, 64, 96, 256, 992])
+def test_mxfp8_forward_small(N, d):
+    w, codes = _mx_inputs(1, 2, N, d, seed=N + d)
+    o, lse = _run(codes, w.scale)
+    _check(codes, o, lse, w.scale)
+
+
+@pytest.mark.parametrize("q_std", [1.0, 3.0])
+def test_mxfp8_forward_spread_scores(q_std):
+    w, codes = _mx_inputs(2, 2, 1024, 128, seed=77, q_std=q_std)
+    o, lse = _run(codes, w.scale)
+    _check(codes, o, lse, w.scale)
+
+
+def test_mxfp8_forward_headline_shape_sampled():
+    w, codes = _mx_inputs(2, 16, 4096, 128, seed=3)
+    o, lse = _run(codes, w.scale)
+    _check(codes, o, lse, w.scale, heads=[(0, 0), (1, 15), (1, 7)])
+
+
+def test_mxfp8_forward_error_against_unquantized_attention():
+    # Against attention on the unquantized bf16 inputs the error is mostly the
+    # inputs' own E4M3 rounding (relative RMS ~5 % on N(0,1) data, computed
+    # here by the oracle on the dequantized inputs); the kernel's rounding of P
+    # may add only a little on top of it.
+    from oracle import attention_forward
+    w, codes = _mx_inputs(1, 4, 512, 128, seed=5)
+    o, _ = _run(codes, w.scale)
+    x = make_inputs(w)
+    ro, _ = attention_forward(*(to_f64(x[n]) for n in ("q", "k", "v")), w.scale)
+    rq, _ = attention_forward_mxfp8(*codes, w.scale)
+
+    def rel(a):
+        return np.sqrt(np.mean((a - ro) ** 2)) / np.sqrt(np.mean(ro ** 2))
+
+    assert rel(rq) < 0.08, f"format error {rel(rq):.3f}"
+    assert rel(o) <= 1.25 * rel(rq), f"kernel {rel(o):.3f} against format {rel(rq):.3f}"

@@ -16,6 +16,7 @@ import os
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
            "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_matmul_nt",
+           "attn_quantize_mxfp8", "attn_fwd_mxfp8",
            "library", "AttnError",
            "ATTN_BF16", "ATTN_FP32", "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "LIB_PATH"]
 
@@ -68,6 +69,12 @@ def library():
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                              ctypes.c_size_t, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int, c_vp]
+    lib.attn_quantize_mxfp8.restype = ctypes.c_int
+    lib.attn_quantize_mxfp8.argtypes = [c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_vp, c_vp, ctypes.c_int,
+                                        c_vp]
+    lib.attn_fwd_mxfp8.restype = ctypes.c_int
+    lib.attn_fwd_mxfp8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
+                                   c_i64, c_f, c_vp]
     lib.attn_matmul_nt.restype = ctypes.c_int
     lib.attn_matmul_nt.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_vp]
     lib.attn_bwd_ex.restype = ctypes.c_int
@@ -321,3 +328,60 @@ def attn_matmul_nt(a, b, *, out=None, stream=None):
                                 _stream(a.device, stream))
     _check(st)
     return out
+
+
+def attn_quantize_mxfp8(x, *, transpose=False, stream=None):
+    """MXFP8 codes and scales (uint8 tensors) of bf16 x [..., rows, cols] (see attn_quantize_mxfp8).
+
+    transpose=False: codes like x, scales [..., rows, cols/32]; transpose=True:
+    codes [..., cols, rows], scales [..., cols, rows/32].
+    """
+    import torch
+    lib = library()
+    if x.dim() < 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous tensor [..., rows, cols]")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a GPU device")
+    lead = tuple(x.shape[:-2])
+    rows, cols = x.shape[-2], x.shape[-1]
+    batch = 1
+    for n in lead:
+        batch *= n
+    if transpose:
+        q = torch.empty(lead + (cols, rows), dtype=torch.uint8, device=x.device)
+        sc = torch.empty(lead + (cols, max(rows // 32, 0)), dtype=torch.uint8, device=x.device)
+    else:
+        q = torch.empty(lead + (rows, cols), dtype=torch.uint8, device=x.device)
+        sc = torch.empty(lead + (rows, max(cols // 32, 0)), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        st = lib.attn_quantize_mxfp8(_ptr(x), batch, rows, cols, 1 if transpose else 0, _ptr(q), _ptr(sc),
+                                     _dtype_code(x), _stream(x.device, stream))
+    _check(st)
+    return q, sc
+
+
+def attn_fwd_mxfp8(q8, q_scales, k8, k_scales, vt8, vt_scales, scale=None, *, out=None, lse=None,
+                   stream=None):
+    """O (bf16), LSE of MXFP8 attention (see attn_fwd_mxfp8). q8, k8 [B,H,N,d]; vt8 [B,H,d,N]."""
+    import torch
+    lib = library()
+    B, H, N, d = q8.shape
+    shapes = {"q8": (q8, (B, H, N, d)), "q_scales": (q_scales, (B, H, N, d // 32)),
+              "k8": (k8, (B, H, N, d)), "k_scales": (k_scales, (B, H, N, d // 32)),
+              "vt8": (vt8, (B, H, d, N)), "vt_scales": (vt_scales, (B, H, d, N // 32))}
+    for name, (t, shp) in shapes.items():
+        if tuple(t.shape) != shp or t.dtype != torch.uint8 or not t.is_contiguous() or t.device != q8.device:
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {shp} on {q8.device}")
+    if q8.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    with torch.cuda.device(q8.device):
+        st = lib.attn_fwd_mxfp8(_ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales), _ptr(vt8), _ptr(vt_scales),
+                                _ptr(out), _ptr(lse), B, H, N, d, float(scale), _stream(q8.device, stream))
+    _check(st)
+    return out, lse

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtiledattn.so")
-SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "matmul.hip"]
+SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "matmul.hip", "attn_fp8.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -280,6 +280,70 @@ attn_status attn_matmul_nt(const void* a, const void* b, void* c, int64_t M, int
   return ok();
 }
 
+attn_status attn_quantize_mxfp8(const void* x, int64_t batch, int64_t rows, int64_t cols, int transpose,
+                                void* q, void* scales, attn_dtype dtype, void* stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "MXFP8 quantization takes bf16 input only");
+  if (batch < 0 || rows < 0 || cols < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "negative size (batch=%lld rows=%lld cols=%lld)", (long long)batch,
+                (long long)rows, (long long)cols);
+  if (transpose != 0 && transpose != 1)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "transpose must be 0 or 1 (got %d)", transpose);
+  const int64_t blocked = transpose ? rows : cols;
+  if (blocked % 32 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "the blocked dimension (%s=%lld) must be a multiple of 32",
+                transpose ? "rows" : "cols", (long long)blocked);
+  if (rows > INT32_MAX || cols > INT32_MAX || (rows && cols && batch > (INT64_MAX / 4) / rows / cols))
+    return fail(ATTN_ERR_UNSUPPORTED, "input too large");
+  const int64_t elems = batch * rows * cols;
+  if (elems == 0) return ok();
+  attn_status s;
+  if ((s = check_ptr(x, "x", 16)) != ATTN_OK || (s = check_ptr(q, "q", 16)) != ATTN_OK ||
+      (s = check_ptr(scales, "scales", 1)) != ATTN_OK)
+    return s;
+  const Range in = {"x", (uintptr_t)x, (uintptr_t)x + (uintptr_t)elems * 2};
+  const Range out[2] = {{"q", (uintptr_t)q, (uintptr_t)q + (uintptr_t)elems},
+                        {"scales", (uintptr_t)scales, (uintptr_t)scales + (uintptr_t)(elems / 32)}};
+  for (const Range& o : out)
+    if (overlaps(o, in)) return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input x", o.name);
+  if (overlaps(out[0], out[1])) return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs q and scales overlap");
+  const hipError_t he = tattn::launch_mx_quantize(x, batch, rows, cols, transpose == 1, q, scales, stream);
+  if (he != hipSuccess) return fail(ATTN_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(he));
+  return ok();
+}
+
+attn_status attn_fwd_mxfp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales,
+                           const void* vt8, const void* vt_scales, void* o, float* lse, int64_t B,
+                           int64_t H, int64_t N, int64_t d, float scale, void* stream) {
+  int64_t elems = 0, rows = 0;
+  attn_status s = check_shape(B, H, N, d, ATTN_BF16, &elems, &rows);
+  if (s != ATTN_OK) return s;
+  if ((s = check_scale(scale)) != ATTN_OK) return s;
+  if (N % 32 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "N=%lld must be a multiple of 32 (the 32-key scale blocks of V^T)",
+                (long long)N);
+  if (rows == 0) return ok();
+  const struct { const void* p; const char* n; uintptr_t align, bytes; } ins[] = {
+      {q8, "q8", 16, (uintptr_t)elems}, {q_scales, "q_scales", 4, (uintptr_t)elems / 32},
+      {k8, "k8", 16, (uintptr_t)elems}, {k_scales, "k_scales", 4, (uintptr_t)elems / 32},
+      {vt8, "vt8", 16, (uintptr_t)elems}, {vt_scales, "vt_scales", 4, (uintptr_t)elems / 32}};
+  for (auto& x : ins)
+    if ((s = check_ptr(x.p, x.n, x.align)) != ATTN_OK) return s;
+  if ((s = check_ptr(o, "o", 16)) != ATTN_OK || (s = check_ptr(lse, "lse", 16)) != ATTN_OK) return s;
+  const Range out[2] = {{"o", (uintptr_t)o, (uintptr_t)o + (uintptr_t)elems * 2},
+                        {"lse", (uintptr_t)lse, (uintptr_t)lse + (uintptr_t)rows * 4}};
+  for (const Range& r : out)
+    for (auto& x : ins)
+      if (overlaps(r, Range{x.n, (uintptr_t)x.p, (uintptr_t)x.p + x.bytes}))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", r.name, x.n);
+  if (overlaps(out[0], out[1])) return fail(ATTN_ERR_INVALID_ARGUMENT, "outputs o and lse overlap");
+  tattn::Fp8Args a{q8, q_scales, k8, k_scales, vt8, vt_scales, o, lse, B * H, N, d, scale, stream};
+  const hipError_t he = tattn::launch_attn_fwd_mxfp8(a);
+  if (he != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(he));
+  return ok();
+}
+
 attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t B,
                        int64_t H, int64_t N, int64_t d, void* o, float* lse, attn_dtype dtype,
                        void* stream) {

@@ -82,6 +82,30 @@ struct BwdArgs {
 };
 
 hipError_t launch_attn_fwd(const FwdArgs& a);
+
+// MXFP8 forward: E4M3 Q, K [BH, N, d] with scales [BH, N, d/32], V^T [BH, d, N]
+// with scales [BH, d, N/32]; O bf16 [BH, N, d], LSE [BH, N].
+struct Fp8Args {
+  const void* q8;
+  const void* qs;
+  const void* k8;
+  const void* ks;
+  const void* vt8;
+  const void* vts;
+  void* o;
+  float* lse;
+  int64_t BH;
+  int64_t N;
+  int64_t d;
+  float scale;
+  void* stream;
+};
+hipError_t launch_attn_fwd_mxfp8(const Fp8Args& a);
+// MXFP8 quantizer: x [batch, rows, cols] bf16 -> q, sc; transpose = false:
+// q [batch, rows, cols], sc [batch, rows, cols/32]; transpose = true:
+// q [batch, cols, rows], sc [batch, cols, rows/32].
+hipError_t launch_mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, bool transpose,
+                              void* q, void* sc, void* stream);
 // C = A B^T, bf16: A [M, K], B [N, K], C [M, N].
 hipError_t launch_matmul_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
                             void* stream);

@@ -22,6 +22,7 @@ MI355X_PEAK_FLOPS = {
     "bf16": 2.5e15,   # dense MFMA
     "fp16": 2.5e15,
     "fp32": 157.3e12,  # fp32 matrix
+    "fp8": 5.0e15,     # dense MFMA (E4M3 / MXFP8)
 }
 
 
