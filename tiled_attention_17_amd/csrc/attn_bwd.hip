@@ -10,27 +10,35 @@
 //
 // Three launches on the caller's stream, no atomics (deterministic):
 //   1. row_dot:  D_i = sum_k dO_ik O_ik (memory-bound, one pass over O, dO);
-//   2. dkdv:     one workgroup per 32*NW keys; each wave keeps its 32 keys of
-//                K and V in VGPRs and sweeps all query tiles (64 queries per
-//                step, Q/dO/LSE/D staged in LDS, double-buffered), computing
-//                S = Q K^T and dP = dO V^T with the key in the lane (MFMA C
-//                layout) so that P and dS feed dV^T += dO^T P and
-//                dK^T += Q^T dS directly as B operands; dO^T and Q^T come from
-//                ds_read_b64_tr_b16 transposed LDS reads;
-//   3. dq:       one workgroup per 32*NW queries; each wave keeps Q and dO of
-//                its 32 queries in VGPRs and sweeps all key tiles, computing
-//                S^T = K Q^T and dP^T = V dO^T with the query in the lane, then
-//                dQ^T += K^T dS^T (K^T via transposed LDS reads).
-// The recomputation of S, P and dP in both sweeps trades extra MFMA work for
+//   2. dkdv:     one workgroup per 128 keys; each wave keeps K^T and V^T of
+//                its 32 keys in VGPRs and sweeps the query tiles (64 queries
+//                per step, Q/dO/LSE/D staged in LDS, double-buffered),
+//                computing S = Q K^T and dP = dO V^T with the key in the lane
+//                so that P and dS feed dV^T += dO^T P and dK^T += Q^T dS as B
+//                operands; dO^T and Q^T come from ds_read_b64_tr_b16
+//                transposed LDS reads;
+//   3. dq:       one workgroup per 256 queries; each wave keeps Q^T and dO^T
+//                of its 32 queries in VGPRs and sweeps the key tiles,
+//                computing S^T = K Q^T and dP^T = V dO^T with the query in
+//                the lane, then dQ^T += K^T dS^T.
+// The dQ sweep uses the forward's tile shapes (tile_common.h): K and V go
+// straight to LDS with buffer_load ... lds, K^T is transposed in registers
+// while staging, so every MFMA operand read is one ds_read_b128. (The same
+// treatment of the dK/dV sweep, with Q^T and dO^T transposed while staging,
+// measured 2 % slower there: that kernel runs one wave per SIMD and is bound
+// by its serial vector work, not by the transposed reads.) The
+// recomputation of S, P and dP in both sweeps trades extra MFMA work for
 // never storing dS or taking atomics on dQ.
 #include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "tile_common.h"
 
 namespace tattn {
 
-constexpr int kBwdBlk = 64;  // rows per streamed tile (queries in dkdv, keys in dq)
+constexpr int kBwdBlk = 64;  // queries per streamed tile of the dK/dV sweep
+
 
 // ---------------------------------------------------------------------------
 // 1. D_i = dO_i . O_i
@@ -266,31 +274,60 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-struct DqCfg {
+// One workgroup per 256 queries: 8 waves of 32 queries, two per SIMD. Each
+// wave keeps Q^T and dO^T of its queries in VGPRs (B operands) and sweeps the
+// key tiles of 64 keys, with the query in the lane throughout:
+//   S^T = K Q^T and dP^T = V dO^T   (K, V row-major in LDS, as the forward's
+//                                     K tile: rows at swap23(key), chunks
+//                                     swizzled; staged with buffer_load ... lds)
+//   P^T = 2^(c S^T - LSE2), dS^T = P^T (dP^T - D)   (LSE2 and D per lane)
+//   dQ^T += K^T dS^T                 (K^T staged transposed in LDS, as the
+//                                     forward's V^T tile, by a register
+//                                     transpose; read with ds_read_b128)
+// so every MFMA operand read is one ds_read_b128 and no transposed LDS read
+// is needed. dQ = scale dQ^T^T at the end.
+template <int D>
+struct DqTile {
+  static constexpr int NW = 8;
   static constexpr int BM = 32 * NW;
-  static constexpr int BN = kBwdBlk;
-  static constexpr int PITCH = D + 8;
-  static constexpr int TILE = BN * PITCH;
-  static constexpr int THREADS = NW * 64;
-  static constexpr int CHUNKS = BN * D / 8;
-  static constexpr int CPT = CHUNKS / THREADS;
-  static constexpr int DK = D / 16;
-  static constexpr int DB = D / 32;
-  static_assert(CHUNKS % THREADS == 0, "tile must split evenly");
+  using T = FwdTile<D, 64>;
+  static constexpr int STAGE = 3 * T::KTILE;  // K rows, V rows, K^T
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16* __restrict__ dQ, int Nq, int Nk, int BH, int n_qtiles, int total_tiles, float c,
-    float scale, int causal, int remap) {
-  using C = DqCfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * C::TILE];
-  // stage b: K tile at smem + 2 b TILE, V tile right after it
-  auto ks = [&](int b) { return smem + 2 * b * C::TILE; };
-  auto vs = [&](int b) { return smem + (2 * b + 1) * C::TILE; };
+template <bool MASKED, int D>
+__device__ __forceinline__ void dq_scores_to_ds(const f32x16* sacc, const f32x16* dpacc, float c,
+                                                float lse2, float drow, int key0, int kmax, int h,
+                                                u32x4* pw) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      // slot i of block kb: key key0 + 32 kb + 16 (i/8) + 8 h + i%8
+      float p0 = fast_exp2(fmaf(sacc[kb][i], c, -lse2));
+      float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -lse2));
+      if (MASKED) {
+        const int k = key0 + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7);
+        p0 = k > kmax ? 0.f : p0;
+        p1 = k + 1 > kmax ? 0.f : p1;
+      }
+      pw[2 * kb + (i >> 3)][(i & 7) >> 1] =
+          pack_bf16x2(p0 * (dpacc[kb][i] - drow), p1 * (dpacc[kb][i + 1] - drow));
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                        const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                        const float* __restrict__ LSE, const float* __restrict__ Dv,
+                        bf16* __restrict__ dQ, int Nq, int Nk, int BH, int n_qtiles, int total_tiles,
+                        float c, float scale, int causal, int remap) {
+  using C = DqTile<D>;
+  using T = typename C::T;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  auto ks = [&](int b) { return smem + b * C::STAGE; };
+  auto vs = [&](int b) { return smem + b * C::STAGE + T::KTILE; };
+  auto kts = [&](int b) { return smem + b * C::STAGE + 2 * T::KTILE; };
 
   // Causal launches take the query tiles that see the most keys (the last
   // ones) first; others keep one head's tiles on one XCD.
@@ -307,6 +344,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
   bh = __builtin_amdgcn_readfirstlane(bh);
   qt = __builtin_amdgcn_readfirstlane(qt);
   const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const bf16* Kh = K + kbase;
+  const bf16* Vh = V + kbase;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(Kh, Nk);
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q_row = qt * C::BM + wave * 32 + lq;
@@ -316,128 +356,69 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
   const int off = Nk - Nq;
   const int q_lo = qt * C::BM, q_hi = min(q_lo + C::BM, Nq) - 1;
   const int lim = causal ? min(Nk, q_hi + off + 1) : Nk;
-  const int n_kt = lim > 0 ? (lim + C::BN - 1) / C::BN : 0;
+  const int n_kt = lim > 0 ? (lim + 63) / 64 : 0;
   const int all_see = causal ? min(Nk, q_lo + off + 1) : Nk;
-  const int n_full = all_see > 0 ? all_see / C::BN : 0;
-  const int kmax = causal ? min(Nk - 1, q_row + off) : Nk - 1;  // last key this lane's query sees
+  const int n_full = all_see > 0 ? all_see / 64 : 0;
+  const int kmax = causal ? min(Nk - 1, q_row + off) : Nk - 1;
 
-  bf16x8 qf[C::DK], dof[C::DK];
-#pragma unroll
-  for (int s = 0; s < C::DK; ++s) {
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (q_ok) {
-      x = *(const u32x4*)(Q + qbase + (size_t)q_row * D + 16 * s + 8 * h);
-      y = *(const u32x4*)(dO + qbase + (size_t)q_row * D + 16 * s + 8 * h);
-    }
-    qf[s] = as_bf16x8(x);
-    dof[s] = as_bf16x8(y);
-  }
+  bf16x8 qf[T::DK], dof[T::DK];
+  load_q<D>(Q + qbase + (size_t)q_row * D, q_ok, h, qf);
+  load_q<D>(dO + qbase + (size_t)q_row * D, q_ok, h, dof);
   // A query that sees no key has LSE = -inf; all its keys are masked.
   const float lse2 = q_ok ? LSE[(size_t)bh * Nq + q_row] * kLog2e : INFINITY;
   const float drow = q_ok ? Dv[(size_t)bh * Nq + q_row] : 0.f;
 
-  u32x4 kreg[C::CPT], vreg[C::CPT];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::THREADS;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8, kk = j * C::BN + row;
-      u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      if (kk < Nk) {
-        a = *(const u32x4*)(K + kbase + (size_t)kk * D + col);
-        b = *(const u32x4*)(V + kbase + (size_t)kk * D + col);
-      }
-      kreg[i] = a;
-      vreg[i] = b;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::THREADS;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *(u32x4*)(ks(buf) + swap23(row) * C::PITCH + col) = kreg[i];
-      *(u32x4*)(vs(buf) + swap23(row) * C::PITCH + col) = vreg[i];
-    }
+  const VtOffsets vo(lq, h);
+  const KOffsets<D, true> ko(lq, h);
+  const KDirect<D, 64, C::NW> kd(0, wave, lane);
+  Stager<D, 64, 512, 64, false> st;  // K^T through registers
+  auto stage_direct = [&](int j, int buf) {
+    kd.load(Kh, Nk, j, 64, ks(buf));
+    kd.load(Vh, Nk, j, 64, vs(buf));
   };
 
-  f32x16 dqacc[C::DB];
+  f32x16 dqacc[T::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  const int g = lane >> 4, j16 = lane & 15;
-  const int tr_col = 16 * (g & 1) + 4 * (j16 & 3);
-  const int tr_row = 4 * h + (j16 >> 2);
-
+  if (n_kt > 0) {
+    stage_direct(0, 0);
+    st.load(krs, krs, 0, 0, 0, tid);
+    st.store(ks(0), kts(0), 0, tid);
+    wait_vmem();
+    __syncthreads();
+  }
   auto step = [&](auto masked, int j) {
     constexpr bool MASKED = decltype(masked)::value;
     const int cur = j & 1;
-    if (j + 1 < n_kt) load_tile(j + 1);
-
-    unsigned dsk[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sacc, dpacc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
-      const bf16* kp = ks(cur) + (32 * kb + lq) * C::PITCH + 8 * h;
-      const bf16* vp = vs(cur) + (32 * kb + lq) * C::PITCH + 8 * h;
-#pragma unroll
-      for (int s = 0; s < C::DK; ++s) {
-        sacc = mfma32x32x16(as_bf16x8(*(const u32x4*)(kp + 16 * s)), qf[s], sacc);
-        dpacc = mfma32x32x16(as_bf16x8(*(const u32x4*)(vp + 16 * s)), dof[s], dpacc);
-      }
-      // slot i holds key j*64 + 32 kb + 16 (i/8) + 8 h + i%8 for query lq.
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float p0 = fast_exp2(fmaf(sacc[i], c, -lse2));
-        float p1 = fast_exp2(fmaf(sacc[i + 1], c, -lse2));
-        if (MASKED) {  // keys past kmax (ragged end or causal window) get P = 0
-          const int k0 = j * C::BN + 32 * kb + 16 * (i >> 3) + 8 * h + (i & 7);
-          p0 = k0 > kmax ? 0.f : p0;
-          p1 = k0 + 1 > kmax ? 0.f : p1;
-        }
-        dsk[kb][i >> 1] = pack_bf16x2(p0 * (dpacc[i] - drow), p1 * (dpacc[i + 1] - drow));
-      }
+    const bool more = j + 1 < n_kt;
+    if (more) {
+      stage_direct(j + 1, cur ^ 1);
+      st.load(krs, krs, j + 1, j + 1, 0, tid);
     }
-
-    // dQ^T += K^T dS^T over 4 steps of 16 keys.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const u32x4 sw = {dsk[t >> 1][4 * (t & 1)], dsk[t >> 1][4 * (t & 1) + 1],
-                        dsk[t >> 1][4 * (t & 1) + 2], dsk[t >> 1][4 * (t & 1) + 3]};
-      const bf16* ktp = ks(cur) + (16 * t + tr_row) * C::PITCH + tr_col;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 a = lds_read_tr_pair(ktp + 32 * db, ktp + 8 * C::PITCH + 32 * db);
-        dqacc[db] = mfma32x32x16(a, as_bf16x8(sw), dqacc[db]);
-      }
-    }
-
-    if (j + 1 < n_kt) store_tile(cur ^ 1);
+    f32x16 sacc[2], dpacc[2];
+    score_tile<D>(ks(cur), qf, ko, sacc);
+    score_tile<D>(vs(cur), dof, ko, dpacc);
+    u32x4 pw[4];
+    dq_scores_to_ds<MASKED, D>(sacc, dpacc, c, lse2, drow, j * 64, kmax, h, pw);
+    if (more) st.store(ks(cur ^ 1), kts(cur ^ 1), 0, tid);
+    pv_tile<D>(kts(cur), pw, vo, dqacc);  // dQ^T += K^T dS^T
+    wait_vmem();
     __syncthreads();
   };
-
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-  // Key tiles from n_full on are masked: at most kMaxMaskedSteps of them
-  // (a BM-query tile's mask edge spans BM - 1 keys plus a ragged end).
+  // Key tiles from n_full on are masked (a 256-query tile's mask edge spans
+  // up to five 64-key tiles; they run in a loop of their own).
   const int n_plain = min(n_full, n_kt);
   int j = 0;
   for (; j < n_plain; ++j) step(std::false_type{}, j);
-#pragma unroll
-  for (int m = 0; m < kMaxMaskedSteps; ++m)
-    if (j < n_kt) step(std::true_type{}, j++);
+  for (; j < n_kt; ++j) step(std::true_type{}, j);
 
   if (q_ok) {
     bf16* row = dQ + qbase + (size_t)q_row * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < T::DB; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         u32x2 w;
@@ -479,11 +460,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (rows > 0) {
-    constexpr int NW = 4;
-    const int n_qt = (int)((a.Nq + 32 * NW - 1) / (32 * NW));
+    constexpr int BM = DqTile<D>::BM;
+    const int n_qt = (int)((a.Nq + BM - 1) / BM);
     const int64_t total = a.BH * n_qt;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)total), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
                        a.lse, a.row_dot, (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH, n_qt,
                        (int)total, c, a.scale, a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
