@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) + % of MI355X bf16 MFMA peak, N=4096 d=128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_17_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "device_common.h")]
+                  for f in ("attn_fwd.hip", "tile_common.h", "device_common.h")]
 
 
 def kernel_source_digest():

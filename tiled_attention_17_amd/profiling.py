@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 
 FWD_KERNEL = "attn_fwd_bf16_pingpong_kernel"
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_17_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "device_common.h")]
+                  for f in ("attn_fwd.hip", "tile_common.h", "device_common.h")]
 
 
 def source_digest():
