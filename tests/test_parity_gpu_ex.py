@@ -311,7 +311,7 @@ def _check_bwd(x, dq, dk, dv, scale, causal, heads=None):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Nq,Nk", [(1, 1), (64, 64), (200, 200), (513, 513), (100, 700), (700, 100),
-                                   (300, 129), (1, 1000)])
+                                   (300, 129), (1, 1000), (777, 1100), (1100, 777), (1536, 1536)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_ex_small(Nq, Nk, d, causal):
     w = _wl(1, 2, Nq, Nk, d, seed=60 + Nq + Nk + d)

@@ -10,25 +10,26 @@
 //
 // Three launches on the caller's stream, no atomics (deterministic):
 //   1. row_dot:  D_i = sum_k dO_ik O_ik (memory-bound, one pass over O, dO);
-//   2. dkdv:     one workgroup per 128 keys; each wave keeps K^T and V^T of
-//                its 32 keys in VGPRs and sweeps the query tiles (64 queries
-//                per step, Q/dO/LSE/D staged in LDS, double-buffered),
-//                computing S = Q K^T and dP = dO V^T with the key in the lane
-//                so that P and dS feed dV^T += dO^T P and dK^T += Q^T dS as B
-//                operands; dO^T and Q^T come from ds_read_b64_tr_b16
-//                transposed LDS reads;
+//   2. dkdv:     one workgroup per 256 keys; each wave keeps K^T of its 32
+//                keys in VGPRs, the workgroup keeps the V rows of its keys
+//                in LDS, and the query tiles stream through LDS (64 queries
+//                per stage, two sub-steps of 32), computing S = Q K^T and
+//                dP = dO V^T with the key in the lane so that P and dS feed
+//                dV^T += dO^T P and dK^T += Q^T dS as B operands; dO^T and
+//                Q^T come from ds_read_b64_tr_b16 transposed reads of the
+//                row-major tiles;
 //   3. dq:       one workgroup per 256 queries; each wave keeps Q^T and dO^T
 //                of its 32 queries in VGPRs and sweeps the key tiles,
 //                computing S^T = K Q^T and dP^T = V dO^T with the query in
 //                the lane, then dQ^T += K^T dS^T.
-// The dQ sweep uses the forward's tile shapes (tile_common.h): K and V go
-// straight to LDS with buffer_load ... lds, K^T is transposed in registers
-// while staging, so every MFMA operand read is one ds_read_b128. (The same
-// treatment of the dK/dV sweep, with Q^T and dO^T transposed while staging,
-// measured 2 % slower there: that kernel runs one wave per SIMD and is bound
-// by its serial vector work, not by the transposed reads.) The
-// recomputation of S, P and dP in both sweeps trades extra MFMA work for
-// never storing dS or taking atomics on dQ.
+// Both sweeps run two waves per SIMD and stage tiles with buffer_load ...
+// lds (tile_common.h). The dQ sweep uses the forward's tile shapes: K^T is
+// transposed in registers while staging, so every MFMA operand read is one
+// ds_read_b128. The dK/dV sweep reads its transposed operands with
+// transposed LDS reads instead, under a chunk swizzle that keeps both read
+// kinds free of bank conflicts. The recomputation of S, P and dP in both
+// sweeps trades extra MFMA work for never storing dS or taking atomics on
+// dQ.
 #include <type_traits>
 
 #include "device_common.h"
@@ -37,7 +38,6 @@
 
 namespace tattn {
 
-constexpr int kBwdBlk = 64;  // queries per streamed tile of the dK/dV sweep
 
 
 // ---------------------------------------------------------------------------
@@ -67,39 +67,47 @@ __global__ __launch_bounds__(256) void attn_bwd_rowdot_kernel(const bf16* __rest
 // ---------------------------------------------------------------------------
 // 2. dK, dV
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-struct DkdvCfg {
-  static constexpr int BKV = 32 * NW;          // keys per workgroup
-  static constexpr int BQ = kBwdBlk;           // queries per step
-  static constexpr int PITCH = D + 8;
-  static constexpr int TILE = BQ * PITCH;
-  static constexpr int THREADS = NW * 64;
-  static constexpr int CHUNKS = BQ * D / 8;
-  static constexpr int CPT = CHUNKS / THREADS;
+// One workgroup per 256 keys: 8 waves of 32 keys, two per SIMD. Each wave
+// keeps K^T of its keys in VGPRs (a B operand); the V rows of the
+// workgroup's keys sit in LDS for the whole sweep. The query tiles stream
+// through LDS in stages of 64 (Q and dO rows by buffer_load ... lds,
+// double-buffered), each processed as two sub-steps of 32 queries with the
+// key in the lane:
+//   S = Q K^T and dP = dO V^T         (Q, dO rows as A operands; K^T from
+//                                      VGPRs, V rows from LDS as B operands)
+//   P = 2^(c S - LSE2), dS = P (dP - D)  (LSE2 and D per accumulator slot)
+//   dV^T += dO^T P and dK^T += Q^T dS  (dO^T and Q^T by transposed reads,
+//                                      ds_read_b64_tr_b16, of the same tiles)
+// The tiles use the transposable chunk swizzle kswz<D, 1>, under which both
+// the row reads and the transposed reads are free of bank conflicts. Key r
+// of a wave's 32 sits at LDS row swap23(r), so lane lq owns key
+// 32 wave + swap23(lq) and K^T is loaded in that order.
+// ceil(x / m) for m > 0, and 0 for x <= 0.
+__device__ __forceinline__ int ceil_div_nonneg(int x, int m) { return x > 0 ? (x + m - 1) / m : 0; }
+
+template <int D>
+struct DkdvTile {
+  static constexpr int NW = 8;
+  static constexpr int BKV = 32 * NW;   // keys per workgroup
+  static constexpr int BQ = 64;         // queries per stage
+  static constexpr int QTILE = BQ * D;  // one Q or dO stage, bf16 elements
   static constexpr int DK = D / 16;
   static constexpr int DB = D / 32;
-  static_assert(CHUNKS % THREADS == 0, "tile must split evenly");
 };
 
-// Query tiles a dK/dV workgroup needs under the causal mask (query i sees
-// key j iff j <= i + Nk - Nq): from the first query that sees the tile's
-// first key; tiles before j_full hold a (query, key) pair the mask hides.
-// A key tile's mask edge spans at most BKV - 1 + BQ - 1 query positions, so
-// at most kMaxMaskedSteps query tiles are masked (3 for 128 keys, 64 queries).
-constexpr int kMaxMaskedSteps = 3;
-
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int BH, int n_ktiles,
-    int total_tiles, float c, float scale, int causal, int remap) {
-  using C = DkdvCfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * C::TILE];
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                          const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                          const float* __restrict__ LSE, const float* __restrict__ Dv,
+                          bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int BH,
+                          int n_ktiles, int total_tiles, float c, float scale, int causal, int remap) {
+  using C = DkdvTile<D>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[C::BKV * D + 4 * C::QTILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][C::BQ];  // [buf][lse2 | D][query]
-  // stage b: Q tile at smem + 2 b TILE, dO tile right after it
-  auto qs = [&](int b) { return smem + 2 * b * C::TILE; };
-  auto ds = [&](int b) { return smem + (2 * b + 1) * C::TILE; };
+  bf16* const vs = smem;
+  auto qs = [&](int b) { return smem + C::BKV * D + 2 * b * C::QTILE; };
+  auto dos = [&](int b) { return smem + C::BKV * D + (2 * b + 1) * C::QTILE; };
 
   // Causal launches take the key tiles that see the most queries (the
   // first ones) first; others keep one head's tiles on one XCD.
@@ -115,61 +123,59 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
   bh = __builtin_amdgcn_readfirstlane(bh);
   kt = __builtin_amdgcn_readfirstlane(kt);
   const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
-  const int tid = threadIdx.x, lane = tid & 63, lk = lane & 31, h = lane >> 5;
+  const bf16* Qh = Q + qbase;
+  const bf16* dOh = dO + qbase;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int key = kt * C::BKV + wave * 32 + lk;  // the key this lane owns
+  const int kw_lo = kt * C::BKV + 32 * wave;  // this wave's first key
+  const int key = kw_lo + swap23(lq);         // the key this lane owns
   const bool k_ok = key < Nk;
   const int off = Nk - Nq;
-  const int k_lo = kt * C::BKV, k_hi = min(k_lo + C::BKV, Nk) - 1;
-  const int j0 = causal ? max(0, k_lo - off) / C::BQ : 0;
-  const int j_full = causal ? max(0, (k_hi - off + C::BQ - 1) / C::BQ) : 0;
+  const int n_st = (Nq + C::BQ - 1) / C::BQ;
+  // Under the causal mask the first stage is the one holding the first
+  // query that sees the workgroup's first key.
+  const int j0 = causal ? max(0, kt * C::BKV - off) / C::BQ : 0;
 
-  // K^T and V^T as B operands: lane (key lk, half h) holds d = 16 s + 8 h .. +7.
-  bf16x8 kf[C::DK], vf[C::DK];
-#pragma unroll
-  for (int s = 0; s < C::DK; ++s) {
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (k_ok) {
-      x = *(const u32x4*)(K + kbase + (size_t)key * D + 16 * s + 8 * h);
-      y = *(const u32x4*)(V + kbase + (size_t)key * D + 16 * s + 8 * h);
-    }
-    kf[s] = as_bf16x8(x);
-    vf[s] = as_bf16x8(y);
-  }
+  // V rows of the workgroup's keys (rows >= Nk read as zeros), once.
+  const KDirect<D, C::BKV, C::NW, 1> vd(0, wave, lane);
+  vd.load(V + kbase, Nk, kt, C::BKV, vs);
+  const KDirect<D, C::BQ, C::NW, 1> qd(0, wave, lane);
+  bf16x8 kf[C::DK];
+  load_q<D>(K + kbase + (size_t)key * D, k_ok, h, kf);
 
-  u32x4 qreg[C::CPT], dreg[C::CPT];
   float sreg = 0.f;
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::THREADS;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8, q = j * C::BQ + row;
-      u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      if (q < Nq) {
-        a = *(const u32x4*)(Q + qbase + (size_t)q * D + col);
-        b = *(const u32x4*)(dO + qbase + (size_t)q * D + col);
-      }
-      qreg[i] = a;
-      dreg[i] = b;
-    }
+  auto stage = [&](int j, int buf) {
+    qd.load(Qh, Nq, j, C::BQ, qs(buf));
+    qd.load(dOh, Nq, j, C::BQ, dos(buf));
     if (tid < 2 * C::BQ) {
-      const int q = j * C::BQ + (tid % C::BQ);
+      const int q = j * C::BQ + (tid & (C::BQ - 1));
       if (tid < C::BQ)
         sreg = q < Nq ? LSE[(size_t)bh * Nq + q] * kLog2e : INFINITY;  // P = 0 past Nq
       else
         sreg = q < Nq ? Dv[(size_t)bh * Nq + q] : 0.f;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::THREADS;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *(u32x4*)(qs(buf) + swap23(row) * C::PITCH + col) = qreg[i];
-      *(u32x4*)(ds(buf) + swap23(row) * C::PITCH + col) = dreg[i];
-    }
-    if (tid < 2 * C::BQ) stat[buf][tid / C::BQ][tid % C::BQ] = sreg;
+  auto store_stats = [&](int buf) {
+    if (tid < 2 * C::BQ) stat[buf][tid / C::BQ][tid & (C::BQ - 1)] = sreg;
   };
+
+  // Transposed reads: in each group of 16 lanes, lane 4e + g addresses the
+  // 4 values d = 32 db + 16 ((lane >> 4) & 1) + 4 g .. + 3 of query
+  // 16 t + 8 h + 4 e2 + e; lane j of the group then holds d = 32 db + lq
+  // for 4 consecutive queries. With the swizzle's chunk bits below the row
+  // bits, the offset for block db is the one for db = 0 XOR 32 db.
+  int troff[2][C::DB];
+  {
+    const int g = lane & 3, e = (lane >> 2) & 3, clo = 2 * ((lane >> 4) & 1) + (g >> 1);
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int r = swap23(8 * h + 4 * e2 + e);
+      const int base = r * D + 8 * (clo ^ kswz<D, 1>(r)) + 4 * (g & 1);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) troff[e2][db] = base ^ (32 * db);
+    }
+  }
+  const KOffsets<D, true, 1> ko(lq, h);
 
   f32x16 dkacc[C::DB], dvacc[C::DB];
 #pragma unroll
@@ -177,81 +183,121 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dkacc[db][i] = dvacc[db][i] = 0.f;
 
-  const int g = lane >> 4, j16 = lane & 15;
-  const int tr_col = 16 * (g & 1) + 4 * (j16 & 3);
-  const int tr_row = 4 * h + (j16 >> 2);  // LDS row of query 16t + 8h + e is 16t + 4h + e (e < 4)
-
-  const int n_qt = (Nq + C::BQ - 1) / C::BQ;
-  auto step = [&](auto masked, int j) {
+  // Queries 32 u .. 32 u + 31 of stage j held in buffer cur.
+  auto substep = [&](auto masked, int cur, int j, int u) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int cur = j & 1;
-    if (j + 1 < n_qt) load_tile(j + 1);
-
-    unsigned pk[2][8], dsk[2][8];
+    const bf16* qt = qs(cur) + 32 * u * D;
+    const bf16* dt = dos(cur) + 32 * u * D;
+    f32x16 sacc, dpacc;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 sacc, dpacc;
+    for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
-      const bf16* qp = qs(cur) + (32 * qb + lk) * C::PITCH + 8 * h;
-      const bf16* dp = ds(cur) + (32 * qb + lk) * C::PITCH + 8 * h;
+    for (int s = 0; s < C::DK; ++s) {
+      sacc = mfma32x32x16(k_read(qt, ko, s, 0), kf[s], sacc);
+      dpacc = mfma32x32x16(k_read(dt, ko, s, 0), k_read(vs, ko, s, wave), dpacc);
+    }
+    // Issue order: the three reads of step s + 1 between the two MFMAs of
+    // step s (left alone, the scheduler hoists every read and spills).
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int s = 0; s < C::DK; ++s) {
-        sacc = mfma32x32x16(as_bf16x8(*(const u32x4*)(qp + 16 * s)), kf[s], sacc);
-        dpacc = mfma32x32x16(as_bf16x8(*(const u32x4*)(dp + 16 * s)), vf[s], dpacc);
-      }
-      // slot i holds query 32 qb + 16 (i/8) + 8 h + i%8 (of this tile) for key lk.
-      const float* lse2 = stat[cur][0] + 32 * qb + 8 * h;
-      const float* drow = stat[cur][1] + 32 * qb + 8 * h;
+    for (int s = 0; s < C::DK - 1; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // Slot 8 t + e holds query 32 u + 16 t + 8 h + e of the stage.
+    const float* ls = stat[cur][0] + 32 * u + 8 * h;
+    const float* dd = stat[cur][1] + 32 * u + 8 * h;
+    u32x4 pw[2], sw[2];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const int qi = 16 * (i >> 3) + (i & 7);
-        float p0 = fast_exp2(fmaf(sacc[i], c, -lse2[qi]));
-        float p1 = fast_exp2(fmaf(sacc[i + 1], c, -lse2[qi + 1]));
+    for (int t = 0; t < 2; ++t) {
+      const f32x4 l4[2] = {*(const f32x4*)(ls + 16 * t), *(const f32x4*)(ls + 16 * t + 4)};
+      const f32x4 d4[2] = {*(const f32x4*)(dd + 16 * t), *(const f32x4*)(dd + 16 * t + 4)};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int i = 8 * t + e;
+        float p0 = fast_exp2(fmaf(sacc[i], c, -l4[e >> 2][e & 3]));
+        float p1 = fast_exp2(fmaf(sacc[i + 1], c, -l4[e >> 2][(e & 3) + 1]));
         if (MASKED) {  // hidden pairs (key > query + Nk - Nq) get P = 0
-          const int q0 = j * C::BQ + 32 * qb + 8 * h + qi;
+          const int q0 = j * C::BQ + 32 * u + 16 * t + 8 * h + e;
           p0 = key > q0 + off ? 0.f : p0;
           p1 = key > q0 + 1 + off ? 0.f : p1;
         }
-        const float s0 = p0 * (dpacc[i] - drow[qi]);
-        const float s1 = p1 * (dpacc[i + 1] - drow[qi + 1]);
-        pk[qb][i >> 1] = pack_bf16x2(p0, p1);
-        dsk[qb][i >> 1] = pack_bf16x2(s0, s1);
+        pw[t][e >> 1] = pack_bf16x2(p0, p1);
+        sw[t][e >> 1] = pack_bf16x2(p0 * (dpacc[i] - d4[e >> 2][e & 3]),
+                                    p1 * (dpacc[i + 1] - d4[e >> 2][(e & 3) + 1]));
       }
+      __builtin_amdgcn_sched_barrier(0);  // one half's statistics live at a time
     }
-
-    // dV^T += dO^T P and dK^T += Q^T dS over 4 steps of 16 queries.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const u32x4 pw = {pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1],
-                        pk[t >> 1][4 * (t & 1) + 2], pk[t >> 1][4 * (t & 1) + 3]};
-      const u32x4 sw = {dsk[t >> 1][4 * (t & 1)], dsk[t >> 1][4 * (t & 1) + 1],
-                        dsk[t >> 1][4 * (t & 1) + 2], dsk[t >> 1][4 * (t & 1) + 3]};
-      const bf16* dtp = ds(cur) + (16 * t + tr_row) * C::PITCH + tr_col;
-      const bf16* qtp = qs(cur) + (16 * t + tr_row) * C::PITCH + tr_col;
+    for (int t = 0; t < 2; ++t) {
+      const bf16* dtt = dt + 16 * t * D;
+      const bf16* qtt = qt + 16 * t * D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 a = lds_read_tr_pair(dtp + 32 * db, dtp + 8 * C::PITCH + 32 * db);
-        dvacc[db] = mfma32x32x16(a, as_bf16x8(pw), dvacc[db]);
-        const bf16x8 b = lds_read_tr_pair(qtp + 32 * db, qtp + 8 * C::PITCH + 32 * db);
-        dkacc[db] = mfma32x32x16(b, as_bf16x8(sw), dkacc[db]);
+        const bf16x8 a = lds_read_tr_pair(dtt + troff[0][db], dtt + troff[1][db]);
+        dvacc[db] = mfma32x32x16(a, as_bf16x8(pw[t]), dvacc[db]);
+        const bf16x8 b = lds_read_tr_pair(qtt + troff[0][db], qtt + troff[1][db]);
+        dkacc[db] = mfma32x32x16(b, as_bf16x8(sw[t]), dkacc[db]);
       }
     }
-
-    if (j + 1 < n_qt) store_tile(cur ^ 1);
-    __syncthreads();
+    // Two operands (four transposed reads) ahead of the MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * C::DB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
-  if (j0 < n_qt) {
-    load_tile(j0);
-    store_tile(j0 & 1);
-    __syncthreads();
+  if (j0 < n_st) {
+    stage(j0, 0);
+    wait_vmem();
+    store_stats(0);
   }
+  wait_vmem();  // the V rows
+  __syncthreads();
+  // One stage: prefetch the next, the two sub-steps (MODE 0: none of the
+  // wave's pairs visible, 1: the mask edge runs through the stage, 2: all
+  // visible), publish the prefetched stage.
+  auto run_stage = [&](auto mode, int j) {
+    constexpr int MODE = decltype(mode)::value;
+    const int cur = (j - j0) & 1;
+    const bool more = j + 1 < n_st;
+    if (more) stage(j + 1, cur ^ 1);
+    if (MODE != 0) {
+#pragma unroll 1
+      for (int u = 0; u < 2; ++u) substep(std::integral_constant<bool, MODE == 1>{}, cur, j, u);
+    }
+    if (more) store_stats(cur ^ 1);
+    wait_vmem();
+    __syncthreads();
+  };
+  // This wave's stages run in three phases, each a loop of one kind (no
+  // branch inside a loop body, which would make the accumulators' live
+  // ranges fork): stages before j_vis hold no visible pair, stages from
+  // j_all on hold only visible pairs, and the mask edge of 32 keys crosses
+  // at most two 64-query stages in between. Every wave runs every stage's
+  // barrier.
+  int j_vis = j0, j_all = j0;
+  if (kw_lo >= Nk) {
+    j_vis = j_all = max(j0, n_st);
+  } else if (causal) {
+    // first stage with a visible pair: 64 j + 63 + off >= kw_lo;
+    // first stage with all pairs visible: 64 j + off >= kw_lo + 31
+    j_vis = min(max(j0, ceil_div_nonneg(kw_lo - off - (C::BQ - 1), C::BQ)), max(j0, n_st));
+    j_all = min(max(j_vis, ceil_div_nonneg(kw_lo + 31 - off, C::BQ)), max(j0, n_st));
+  }
+  j_vis = __builtin_amdgcn_readfirstlane(j_vis);
+  j_all = __builtin_amdgcn_readfirstlane(j_all);
   int j = j0;
-#pragma unroll
-  for (int m = 0; m < kMaxMaskedSteps; ++m)
-    if (j < min(j_full, n_qt)) step(std::true_type{}, j++);
-  for (; j < n_qt; ++j) step(std::false_type{}, j);
+  for (; j < j_vis; ++j) run_stage(std::integral_constant<int, 0>{}, j);
+  for (; j < j_all; ++j) run_stage(std::integral_constant<int, 1>{}, j);
+  for (; j < n_st; ++j) run_stage(std::integral_constant<int, 2>{}, j);
 
   if (k_ok) {
     bf16* dkrow = dK + kbase + (size_t)key * D;
@@ -447,11 +493,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (a.Nk > 0) {
-    constexpr int NW = 4;
-    const int n_kt = (int)((a.Nk + 32 * NW - 1) / (32 * NW));
+    constexpr int BKV = DkdvTile<D>::BKV;
+    const int n_kt = (int)((a.Nk + BKV - 1) / BKV);
     const int64_t total = a.BH * n_kt;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)total), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
                        a.lse, a.row_dot, (bf16*)a.dk, (bf16*)a.dv, (int)a.Nq, (int)a.Nk, (int)a.BH,
                        n_kt, (int)total, c, a.scale, a.causal ? 1 : 0,

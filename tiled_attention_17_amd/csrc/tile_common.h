@@ -33,30 +33,43 @@ struct FwdTile {
 // The layout is written lane-linearly by buffer_load ... lds (1 KB per
 // instruction), so no padding is possible and the swizzle is what keeps the
 // reads free of bank conflicts.
-template <int D>
-__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+//
+// SW = 1 is a second swizzle for tiles that are also read transposed
+// (ds_read_b64_tr_b16, the backward's dK/dV sweep): such a read touches, per
+// half wave, rows of 4 consecutive keys (bits 0-1 of r vary) at 4 consecutive
+// logical chunks. SW = 1 permutes the bits of the same row bits so that
+// those 16 (row, chunk) pairs land on 16 distinct chunk positions (D = 128:
+// bits 0-1 of r go to bits 2-3 of the swizzle; D = 64: bit 1 goes to bit 2,
+// and bit 0 already selects the bank half), while 16 consecutive rows still
+// map one-to-one, so both read kinds are free of bank conflicts.
+template <int D, int SW = 0>
+__device__ __forceinline__ int kswz(int r) {
+  if (SW == 0) return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 // Per-lane element offsets of the K operand reads: step s of key block kb
 // (row 32 kb + lq, logical chunk 2 s + h) is at o(s) + 32 kb D, where
 // o(s) = lq D + 8 ((2 s + h) ^ kswz(lq)) = (lq D + 8 (h ^ kswz(lq))) ^ 16 s
 // (the chunk bits sit below the row bits). COMPACT keeps one register and
 // does the XOR per read; otherwise all D / 16 offsets are kept.
-template <int D, bool COMPACT = false>
+template <int D, bool COMPACT = false, int SW = 0>
 struct KOffsets {
   int o[COMPACT ? 1 : D / 16];
   __device__ __forceinline__ KOffsets(int lq, int h) {
     if (COMPACT) {
-      o[0] = lq * D + 8 * (h ^ kswz<D>(lq));
+      o[0] = lq * D + 8 * (h ^ kswz<D, SW>(lq));
     } else {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) o[s] = lq * D + 8 * ((2 * s + h) ^ kswz<D>(lq));
+      for (int s = 0; s < D / 16; ++s) o[s] = lq * D + 8 * ((2 * s + h) ^ kswz<D, SW>(lq));
     }
   }
   __device__ __forceinline__ int at(int s) const { return COMPACT ? (o[0] ^ (16 * s)) : o[s]; }
 };
 
-template <int D, bool COMPACT>
-__device__ __forceinline__ bf16x8 k_read(const bf16* kt, const KOffsets<D, COMPACT>& ko, int s, int kb) {
+template <int D, bool COMPACT, int SW>
+__device__ __forceinline__ bf16x8 k_read(const bf16* kt, const KOffsets<D, COMPACT, SW>& ko, int s,
+                                         int kb) {
   return as_bf16x8(*(const u32x4*)(kt + ko.at(s) + 32 * kb * D));
 }
 
@@ -262,7 +275,7 @@ struct Stager {
 // no VALU work. Completion is waited for with vmcnt before the barrier that
 // publishes the tile.
 
-template <int D, int ROWS, int WAVES = 4>
+template <int D, int ROWS, int WAVES = 4, int SW = 0>
 struct KDirect {
   static constexpr int RPI = 1024 / (2 * D);              // rows per instruction
   static constexpr int NI = ROWS / (WAVES * RPI);         // instructions per wave
@@ -275,7 +288,7 @@ struct KDirect {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int lr = lds_row0 + i * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ kswz<D>(lr);
+      const int c = (lane % CPR) ^ kswz<D, SW>(lr);
       voff[i] = (swap23(lr) * D + 8 * c) * 2;
     }
   }
