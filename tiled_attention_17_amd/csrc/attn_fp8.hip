@@ -29,6 +29,8 @@
 //   * K and V^T tiles (64 keys) go straight to LDS with buffer_load ... lds,
 //     XOR-swizzled by 16-byte chunk so operand reads are conflict-free; the
 //     scale bytes of a tile are staged into LDS beside them.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -307,7 +309,11 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_kt; ++j) {
+  // Only the last tile of a ragged N holds keys past N; the others run a
+  // body without the per-element selects (the compiler would otherwise
+  // if-convert them into every tile).
+  auto body = [&](auto masked_t, int j) {
+    constexpr bool masked = decltype(masked_t)::value;
     const int cur = j & 1;
     if (j + 1 < n_kt) stage(j + 1, cur ^ 1);
     const uint8_t* kt = kt_(cur);
@@ -335,7 +341,6 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
 
     // online softmax (Lecture 17 page §8.3), lazy running max, keys past N masked
     const int key0 = j * T::BN;
-    const bool masked = key0 + T::BN > N;
     if (masked) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
@@ -400,7 +405,11 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
     }
     wait_vmem();  // next tiles written to LDS
     __syncthreads();
-  }
+  };
+  const int n_full = N / T::BN;
+  int j = 0;
+  for (; j < n_full; ++j) body(std::false_type{}, j);
+  if (j < n_kt) body(std::true_type{}, j);
 
   // O = o / l (bf16), LSE = ln 2 (m + log2 l)
   const float l_tot = add_other_half(l_run);
