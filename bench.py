@@ -173,6 +173,35 @@ def measure_ex(ta, pm, dev, stream, n):
     return out
 
 
+def measure_configs(ta, pm, dev, stream, n):
+    """The other forward configurations (not the headline metric).
+
+    fp32 single head (B=1 H=1 N=256 d=64, against the fp32 MFMA peak), the
+    d = 64 multi-head case (B=4 H=8 N=1024) and the long sequence with
+    spread scores (B=1 H=16 N=16384 d=128, Q ~ N(0, 3^2)), each with
+    library-chosen tiles and one launch per step.
+    """
+    import torch
+
+    from tiled_attention_17_amd.workloads import WORKLOADS, make_inputs
+
+    out = {}
+    for w, key in ((WORKLOADS[0], "fp32_small"), (WORKLOADS[1], "d64"), (WORKLOADS[3], "long")):
+        x = {k: t.to(dev) for k, t in make_inputs(w).items()}
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        reps = n if w.N <= 4096 else max(5, n // 10)
+        ms = _time_ms(lambda: ta.attn_fwd(x["q"], x["k"], x["v"], w.scale, out=o, lse=lse), stream,
+                      3 * reps, reps)
+        fl = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
+        dt = "fp32" if w.dtype == "fp32" else "bf16"
+        peak = pm.MI355X_PEAK_FLOPS[dt] / 1e12
+        tf = fl / (ms * 1e-3) / 1e12
+        out[key] = {"workload": w.name, "ms": ms, "tflops": tf, f"pct_of_{dt}_dense_peak": 100.0 * tf / peak}
+        del x, o, lse
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,7 +215,7 @@ def main():
                     help="CPU work budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward figures in 'extra'")
     ap.add_argument("--no-ex", action="store_true",
-                    help="skip the causal / unequal-length / decoding figures in 'extra'")
+                    help="skip the causal / unequal-length / decoding / other-configuration figures in 'extra'")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -275,6 +304,7 @@ def main():
 
     if not args.no_ex:
         extra.update(measure_ex(ta, pm, dev, stream, max(20, K // 4)))
+        extra.update(measure_configs(ta, pm, dev, stream, max(20, K // 4)))
 
     traffic = measured_traffic()
     result = {

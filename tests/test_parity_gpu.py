@@ -91,7 +91,24 @@ def test_fwd_bf16_small(B, H, N, d):
 @pytest.mark.parametrize("d", [64, 128])
 def test_fwd_bf16_tile_configs(waves, d, monkeypatch):
     monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", "1")
     w = _wl(2, 2, 777, d, seed=5, q_std=3.0)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd(x["q"], x["k"], x["v"], w.scale)
+    torch.cuda.synchronize()
+    _check_fwd(x, o, lse, w.scale, BF16_TOL, BF16_REL)
+
+
+@pytest.mark.parametrize("waves", ["2", "4"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 37, 64, 100, 200, 257, 777, 1000])
+def test_fwd_bf16_keys_split_in_workgroup(N, d, waves, monkeypatch):
+    # Two wave groups take the two halves of the key tiles and merge through
+    # LDS: odd tile counts (group 1 idles one step), a ragged last tile, and
+    # N below two tiles (group 1 sees no key) all go through the merge.
+    monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", "2")
+    w = _wl(2, 3, N, d, seed=400 + N + d, q_std=3.0)
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd(x["q"], x["k"], x["v"], w.scale)
     torch.cuda.synchronize()

@@ -130,10 +130,13 @@ def test_causal_ignores_hidden_keys():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("waves", ["2", "4", "8"])
+@pytest.mark.parametrize("waves,ksplit", [("2", "1"), ("4", "1"), ("8", "1"), ("2", "2"), ("4", "2")])
 @pytest.mark.parametrize("Nq,Nk", [(1, 1000), (100, 700), (300, 129), (513, 64), (64, 2048)])
-def test_unequal_lengths_bf16(Nq, Nk, waves, causal, monkeypatch):
+def test_unequal_lengths_bf16(Nq, Nk, waves, ksplit, causal, monkeypatch):
+    # ksplit "2": the keys of a workgroup split between two wave groups
+    # (unmasked launches only; the causal cases take the other kernels)
     monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", ksplit)
     w = _wl(2, 2, Nq, Nk, 128, seed=Nq + Nk, q_std=3.0)
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)

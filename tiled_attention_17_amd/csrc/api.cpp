@@ -125,6 +125,15 @@ int env_waves() {
   return (w == 2 || w == 4 || w == 8) ? w : 0;
 }
 
+// TILED_ATTN_FWD_KSPLIT=1 (never) or 2 (where allowed) overrides the
+// choice of splitting a workgroup's keys between two wave groups.
+int env_ksplit() {
+  const char* s = std::getenv("TILED_ATTN_FWD_KSPLIT");
+  if (!s) return 0;
+  const int k = std::atoi(s);
+  return (k == 1 || k == 2) ? k : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -205,7 +214,8 @@ attn_status fwd_common(const void* q, const void* k, const void* v, void* o, flo
 
   if (cus == 0 && (s = device_cus(&cus)) != ATTN_OK) return s;
   tattn::FwdArgs a{q, k, v, o, lse, bh, Nq, Nk, d, scale, dtype == ATTN_FP32,
-                   mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves()};
+                   mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves(),
+                   env_ksplit()};
   const hipError_t he = tattn::launch_attn_fwd(a);
   if (he != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(he));
   return ok();

@@ -380,6 +380,132 @@ void attn_fwd_bf16_kernel(const FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 forward, keys split inside the workgroup: two groups of NW waves take
+// the same BM = 32 NW queries, group 0 the first half of the key tiles and
+// group 1 the second, each with LDS buffers of its own, in lock step (one
+// barrier per key tile). At the end group 1 hands its running (m, l, o) to
+// group 0 through LDS, and group 0 merges the two partial results exactly as
+// the online update of the Lecture 17 page (§8.3) merges two key blocks:
+// m = max(m0, m1), l = 2^(m0 - m) l0 + 2^(m1 - m) l1, o likewise. For grids
+// of at most one wave per SIMD (few heads, short sequences) this puts a
+// second wave on every SIMD, whose work hides the first one's latencies,
+// without a second launch. Unmasked launches only: the ragged end of the
+// key range is the only masked tile, and it is group 1's last.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(2 * NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
+  using T = FwdTile<D>;
+  constexpr int BM = 32 * NW;
+  constexpr int NE = 16 * T::DB + 2;  // floats one lane hands over: o, m, l
+  static_assert(NW * NE * 64 * 4 <= 4 * T::STAGE * 2, "hand-over must fit the tile buffers");
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * T::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / NW, wave = wave_all - grp * NW;
+  const int gtid = tid - grp * NW * 64;  // thread index within the group
+  auto ks = [&](int b) { return smem + (2 * grp + b) * T::STAGE; };
+  auto vs = [&](int b) { return smem + (2 * grp + b) * T::STAGE + T::KTILE; };
+
+  const TileId ti = decode_tile(p);
+  const bf16* Kh = (const bf16*)p.k + (size_t)ti.bh * p.Nk * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(Kh, p.Nk);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<D>((const bf16*)p.v + (size_t)ti.bh * p.Nk * D, p.Nk);
+  const int q_row = ti.qt * BM + wave * 32 + lq;
+  const bool q_ok = q_row < p.Nq;
+  const KeyRange kr = key_range<T::BN>(p, 0, ti.qt * BM, BM);
+  if (kr.n_tiles == 0) {
+    if (grp == 0) write_empty<D>(p, ti, q_row, q_ok, h);
+    return;
+  }
+  // Group 0 takes tiles [0, n_half), group 1 [n_half, n_kt); both run n_half
+  // steps (group 1's last one idle when n_kt is odd).
+  const int n_kt = kr.n_tiles, n_half = (n_kt + 1) / 2;
+  const int my_first = grp ? n_half : 0, my_n = grp ? n_kt - n_half : n_half;
+  const int t0 = kr.k_begin / T::BN + my_first;  // this group's first key tile
+  const int kmax = row_kmax(p, kr, q_row);
+  const VtOffsets vo(lq, h);
+  const KOffsets<D, true> ko(lq, h);
+
+  bf16x8 qf[T::DK];
+  load_q<D>((const bf16*)p.q + ((size_t)ti.bh * p.Nq + q_row) * D, q_ok, h, qf);
+
+  f32x16 oacc[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const KDirect<D, 64, NW> kd(0, wave, lane);
+  Stager<D, 32, NW * 64, 64, false> st;
+  if (my_n > 0) {
+    kd.load(Kh, p.Nk, t0, 64, ks(0));
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      st.load(krs, vrs, t0, t0, 32 * half, gtid);
+      st.store(ks(0), vs(0), 32 * half, gtid);
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+
+  // Step i of this group: its key tile my_first + i (local LDS buffer i & 1).
+  auto step = [&](auto masked, int i) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int cur = i & 1;
+    const bool more = i + 1 < my_n;
+    if (more) {
+      kd.load(Kh, p.Nk, t0 + i + 1, 64, ks(cur ^ 1));
+      st.load(krs, vrs, t0 + i + 1, t0 + i + 1, 0, gtid);
+    }
+    f32x16 sacc[2];
+    u32x4 pw[4];
+    score_tile<D>(ks(cur), qf, ko, sacc);
+    softmax_tile<MASKED, T::DB>(sacc, p.c, kr.k_begin + (my_first + i) * T::BN, kmax, h, m_run, l_run,
+                                oacc, pw);
+    if (more) {
+      st.store(ks(cur ^ 1), vs(cur ^ 1), 0, gtid);
+      st.load(krs, vrs, t0 + i + 1, t0 + i + 1, 32, gtid);
+    }
+    pv_tile<D>(vs(cur), pw, vo, oacc);
+    if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 32, gtid);
+    wait_vmem();  // K tile written to LDS
+    __syncthreads();
+  };
+  // Only the range's last tile (index n_full of a ragged end, group 1's
+  // last) holds keys past the end. Each group runs n_half barriers.
+  const int n_plain = min(max(kr.n_full - my_first, 0), my_n);
+  int i = 0;
+  for (; i < n_plain; ++i) step(std::false_type{}, i);
+  if (i < my_n) step(std::true_type{}, i++);
+  for (; i < n_half; ++i) __syncthreads();
+
+  // Hand-over: group 1's lane values to LDS ([wave][element][lane]), group 0 merges.
+  float* xb = (float*)smem + (size_t)wave * NE * 64 + lane;
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xb[(16 * db + e) * 64] = oacc[db][e];
+    xb[(NE - 2) * 64] = m_run;
+    xb[(NE - 1) * 64] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float m1 = xb[(NE - 2) * 64], l1 = xb[(NE - 1) * 64];
+  const float m = fmaxf(m_run, m1);
+  const float m_ref = m == -INFINITY ? 0.f : m;  // neither group saw a visible key
+  const float a0 = fast_exp2(m_run - m_ref), a1 = fast_exp2(m1 - m_ref);
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = a0 * oacc[db][e] + a1 * xb[(16 * db + e) * 64];
+  write_result<D>(p, ti, q_row, q_ok, h, oacc, m, a0 * l_run + a1 * l1);
+}
+
+// ---------------------------------------------------------------------------
 // bf16 forward, ping-pong: 8 waves in two groups of 4 (one wave of each group
 // per SIMD). Within a wave the work of one key tile is split into an MFMA
 // phase (S^T of tile j+1 and O^T += V^T P^T of tile j) and a VALU phase
@@ -745,6 +871,23 @@ static hipError_t launch_bf16(const FwdArgs& a, const FwdParams& p, int64_t tota
   return hipGetLastError();
 }
 
+template <int D, int NW>
+static hipError_t launch_bf16_ksplit(const FwdArgs& a, const FwdParams& p, int64_t total) {
+  hipLaunchKernelGGL((attn_fwd_bf16_ksplit_kernel<D, NW>), dim3((unsigned)total), dim3(2 * NW * 64), 0,
+                     (hipStream_t)a.stream, p);
+  return hipGetLastError();
+}
+
+// Whether to split a workgroup's keys between two wave groups: for unmasked
+// launches without key splits on the smaller tiles, when the grid holds at
+// most one wave per SIMD and each group gets at least two 64-key tiles.
+static bool use_ksplit(const FwdArgs& a, int64_t splits, int nw) {
+  if (a.causal || splits != 1 || nw >= 8 || a.ksplit == 1) return false;
+  if (a.ksplit == 2) return true;
+  const int64_t waves_total = a.BH * ((a.Nq + 31) / 32);
+  return waves_total <= 4 * (int64_t)a.num_cus && (a.Nk + 63) / 64 >= 4;
+}
+
 template <int D>
 static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total) {
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)total), dim3(FwdF32Cfg<D>::THREADS), 0,
@@ -807,12 +950,18 @@ hipError_t launch_attn_fwd(const FwdArgs& a) {
   const FwdParams p = make_params(a, 32 * nw, &total);
   if (total > INT32_MAX) return hipErrorInvalidValue;
   hipError_t e;
-  if (a.d == 64)
+  if (use_ksplit(a, splits, nw)) {
+    if (a.d == 64)
+      e = nw == 4 ? launch_bf16_ksplit<64, 4>(a, p, total) : launch_bf16_ksplit<64, 2>(a, p, total);
+    else
+      e = nw == 4 ? launch_bf16_ksplit<128, 4>(a, p, total) : launch_bf16_ksplit<128, 2>(a, p, total);
+  } else if (a.d == 64) {
     e = nw == 8 ? launch_bf16<64, 8>(a, p, total) : nw == 4 ? launch_bf16<64, 4>(a, p, total)
                                                            : launch_bf16<64, 2>(a, p, total);
-  else
+  } else {
     e = nw == 8 ? launch_bf16<128, 8>(a, p, total) : nw == 4 ? launch_bf16<128, 4>(a, p, total)
                                                              : launch_bf16<128, 2>(a, p, total);
+  }
   if (e != hipSuccess || p.n_splits == 1) return e;
   return launch_attn_merge(p.o_part, p.lse_part, p.n_splits, a.BH * a.Nq, a.d, a.o, a.lse, false,
                            a.stream);

@@ -24,6 +24,8 @@ struct FwdArgs {
   void* stream;
   int num_cus;      // compute units of the device (grid sizing)
   int waves;        // 0 = choose; else waves per workgroup of the bf16 kernel (2, 4 or 8)
+  int ksplit;       // 0 = choose; 1 = never; 2 = split the keys between two wave groups of a
+                    // workgroup where the launch allows it (bf16, no mask, no key splits, waves < 8)
 };
 
 // Parameters of one forward kernel launch (kernel argument, by value).
