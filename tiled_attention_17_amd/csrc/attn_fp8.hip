@@ -38,6 +38,12 @@ namespace tattn {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// Marks x as used here (an empty asm reading its registers): work producing
+// x stays above this point, which keeps the compiler from sinking it below
+// a later wait. A plain device function: the host pass of a kernel template
+// must not see the register constraint.
+__device__ __forceinline__ void consume(const f32x16& x) { asm volatile("" ::"v"(x)); }
+
 // ---------------------------------------------------------------------------
 // quantizer
 // ---------------------------------------------------------------------------
@@ -254,8 +260,26 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
     vchunk[i] = (lane % 4) ^ v8swz(r);
     vvoff[i] = r * N + 16 * vchunk[i];
   }
-  auto stage = [&](int j, int buf) {
+  // Staging of tile j into buffer buf in two parts, so that no wait for
+  // memory sits at the start of a step: stage_issue loads the scale bytes
+  // into registers first and then sends K and V^T straight to LDS (the
+  // compiler's wait for the scale loads then leaves the later LDS DMAs in
+  // flight); stage_commit, after the step's work, writes the scale bytes.
+  unsigned ksw = 0, vse = 127;  // this thread's K scale word and V^T scale byte
+  auto stage_issue = [&](int j, int buf) {
     const int k0 = j * T::BN;
+    if (tid < T::BN) {  // scale bytes: K [row][D/32] by LDS row
+      const int key = k0 + 32 * (tid / 32) + kperm(tid % 32);
+      ksw = 0;
+      if (key < N) {
+        if (D == 128) ksw = *(const unsigned*)(KSh + (size_t)key * 4);
+        else ksw = *(const unsigned short*)(KSh + (size_t)key * 2);
+      }
+    }
+    if (tid < 2 * D) {  // V^T [key block][d % 32][d / 32]
+      const int d = tid >> 1, kb = j * 2 + (tid & 1);
+      vse = kb * 32 < N ? VTSh[(size_t)d * (N / 32) + kb] : 127u;
+    }
     const int krem = N > k0 ? (N - k0) * D : 0;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + (size_t)k0 * D), 0, krem, kBufferRsrcWord3);
@@ -269,23 +293,15 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
       const int off = k0 + 16 * vchunk[i] < N ? vvoff[i] : 0x7fffffff;  // keys past N: zeros
       lds_dma16(vr, (bf16*)(vt_(buf) + (wave * VNI + i) * 1024), off);
     }
-    // scale bytes: K [row][D/32] by LDS row; V^T [key block][d % 32][d / 32]
-    if (tid < T::BN) {
-      const int key = k0 + 32 * (tid / 32) + kperm(tid % 32);
-      unsigned w = 0;
-      if (key < N) {
-        if (D == 128) w = *(const unsigned*)(KSh + (size_t)key * 4);
-        else w = *(const unsigned short*)(KSh + (size_t)key * 2);
-      }
-      *(unsigned*)(ks_(buf) + 4 * tid) = w;
-    }
-    for (int u = tid; u < 2 * D; u += 256) {
-      const int d = u >> 1, blk = u & 1;
-      const int kb = j * 2 + blk;
-      const uint8_t e = kb * 32 < N ? VTSh[(size_t)d * (N / 32) + kb] : (uint8_t)127;
-      vs_(buf)[blk * 128 + (d % 32) * 4 + d / 32] = e;
+  };
+  auto stage_commit = [&](int buf) {
+    if (tid < T::BN) *(unsigned*)(ks_(buf) + 4 * tid) = ksw;
+    if (tid < 2 * D) {
+      const int d = tid >> 1, blk = tid & 1;
+      vs_(buf)[blk * 128 + (d % 32) * 4 + d / 32] = (uint8_t)vse;
     }
   };
+  static_assert(2 * D <= 256, "one V^T scale byte per thread");
 
   // operand read offsets (bytes) within a tile
   int kro[2 * T::KS], vro[2];
@@ -305,7 +321,8 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
   float m_run = -INFINITY, l_run = 0.f;
 
   const int n_kt = (N + T::BN - 1) / T::BN;
-  stage(0, 0);
+  stage_issue(0, 0);
+  stage_commit(0);
   wait_vmem();
   __syncthreads();
 
@@ -315,7 +332,7 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
   auto body = [&](auto masked_t, int j) {
     constexpr bool masked = decltype(masked_t)::value;
     const int cur = j & 1;
-    if (j + 1 < n_kt) stage(j + 1, cur ^ 1);
+    if (j + 1 < n_kt) stage_issue(j + 1, cur ^ 1);
     const uint8_t* kt = kt_(cur);
     const uint8_t* vt = vt_(cur);
 
@@ -403,6 +420,13 @@ void attn_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __rest
       const int vsc = (int)((vw >> (8 * db)) & 0xffu);
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pw, oacc[db], 0, 0, 0, vsc, 0, psc);
     }
+    // The step's results are consumed here (an empty asm reading the
+    // accumulators), so that the compiler keeps the step's work above the
+    // waits for the staged tile instead of sinking it below them.
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) consume(oacc[db]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < n_kt) stage_commit(cur ^ 1);
     wait_vmem();  // next tiles written to LDS
     __syncthreads();
   };
