@@ -143,20 +143,24 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   bf16x8 kf[C::DK];
   load_q<D>(K + kbase + (size_t)key * D, k_ok, h, kf);
 
+  // The statistics are loaded before the stage's LDS DMA and used only when
+  // written to LDS after the stage's work: a use right after the load would
+  // make the compiler wait for the DMA issued behind it as well.
   float sreg = 0.f;
   auto stage = [&](int j, int buf) {
-    qd.load(Qh, Nq, j, C::BQ, qs(buf));
-    qd.load(dOh, Nq, j, C::BQ, dos(buf));
     if (tid < 2 * C::BQ) {
       const int q = j * C::BQ + (tid & (C::BQ - 1));
       if (tid < C::BQ)
-        sreg = q < Nq ? LSE[(size_t)bh * Nq + q] * kLog2e : INFINITY;  // P = 0 past Nq
+        sreg = q < Nq ? LSE[(size_t)bh * Nq + q] : INFINITY;  // P = 0 past Nq
       else
         sreg = q < Nq ? Dv[(size_t)bh * Nq + q] : 0.f;
     }
+    qd.load(Qh, Nq, j, C::BQ, qs(buf));
+    qd.load(dOh, Nq, j, C::BQ, dos(buf));
   };
   auto store_stats = [&](int buf) {
-    if (tid < 2 * C::BQ) stat[buf][tid / C::BQ][tid & (C::BQ - 1)] = sreg;
+    if (tid < 2 * C::BQ)
+      stat[buf][tid / C::BQ][tid & (C::BQ - 1)] = tid < C::BQ ? sreg * kLog2e : sreg;
   };
 
   // Transposed reads: in each group of 16 lanes, lane 4e + g addresses the
