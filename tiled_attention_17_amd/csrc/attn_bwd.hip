@@ -344,6 +344,65 @@ struct DqTile {
   static constexpr int STAGE = 3 * T::KTILE;  // K rows, V rows, K^T
 };
 
+// K^T of one 64-key tile through registers, as the forward stages V^T
+// (Stager's V part: each lane loads the same 8 d-values of two adjacent keys
+// and transpose_v_pair turns them into 8 consecutive keys of two d rows),
+// with one buffer resource per tile (from the tile's first row to the end
+// of the head, so rows past N read as zeros) and per-lane offsets fixed for
+// the whole sweep. The address registers then stay live across the loop: a
+// per-tile offset register, reused by the compiler for a later LDS read while
+// the load was in flight, had the next step's first MFMA wait for the whole
+// staged tile.
+template <int D>
+struct KtStager {
+  using T = FwdTile<D, 64>;
+  static constexpr int WAVES = 8;
+  static constexpr int VPASS = 64 / T::VKEYS;
+  static constexpr int VPW = (VPASS + WAVES - 1) / WAVES;
+  u32x4 va[VPW], vb[VPW];
+  int wave_;
+  int off[VPW];  // byte offset of key kv (and kv + 1 at + 2 D) within a tile
+  // Pass (wave + i * WAVES) of VPASS (at d = 64 only waves 0 .. 3 stage).
+  __device__ __forceinline__ bool has_pass(int i) const {
+    return VPASS % WAVES == 0 || wave_ + i * WAVES < VPASS;
+  }
+  __device__ __forceinline__ KtStager(int t) {
+    const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
+    wave_ = __builtin_amdgcn_readfirstlane(wave);
+    const int col = 8 * (r % T::CPR), g = r / T::CPR;
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      const int kv = (wave + i * WAVES) * T::VKEYS + 8 * g + 2 * p;
+      off[i] = (kv * D + col) * 2;
+    }
+  }
+  __device__ __forceinline__ void load(const bf16* kh, int n_rows, int tile) {
+    const int row0 = tile * 64;
+    const int rem = n_rows > row0 ? n_rows - row0 : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kh + (size_t)row0 * D), 0, rem * D * 2, kBufferRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < VPW; ++i)
+      if (has_pass(i)) {
+        va[i] = buffer_load16(r, off[i]);
+        vb[i] = buffer_load16(r, off[i] + 2 * D);
+      }
+  }
+  __device__ __forceinline__ void store(bf16* kt, int t) const {
+    const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
+    const int d0 = 8 * (r % T::CPR) + 2 * p, g = r / T::CPR;
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      if (!has_pass(i)) continue;
+      u32x4 lo, hi;
+      transpose_v_pair(va[i], vb[i], lo, hi);
+      const int slot = (wave + i * WAVES) * T::VKEYS / 8 + g;
+      *(u32x4*)(kt + d0 * 64 + 8 * (slot ^ vt_swz(d0))) = lo;
+      *(u32x4*)(kt + (d0 + 1) * 64 + 8 * (slot ^ vt_swz(d0 + 1))) = hi;
+    }
+  }
+};
+
 template <bool MASKED, int D>
 __device__ __forceinline__ void dq_scores_to_ds(const f32x16* sacc, const f32x16* dpacc, float c,
                                                 float lse2, float drow, int key0, int kmax, int h,
@@ -396,7 +455,6 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
   const bf16* Kh = K + kbase;
   const bf16* Vh = V + kbase;
-  const __amdgpu_buffer_rsrc_t krs = head_rsrc<D>(Kh, Nk);
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q_row = qt * C::BM + wave * 32 + lq;
@@ -421,10 +479,10 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const VtOffsets vo(lq, h);
   const KOffsets<D, true> ko(lq, h);
   const KDirect<D, 64, C::NW> kd(0, wave, lane);
-  Stager<D, 64, 512, 64, false> st;  // K^T through registers
+  KtStager<D> st(tid);  // K^T through registers
   auto stage_direct = [&](int j, int buf) {
-    kd.load(Kh, Nk, j, 64, ks(buf));
-    kd.load(Vh, Nk, j, 64, vs(buf));
+    kd.template load<true>(Kh, Nk, j, 64, ks(buf));
+    kd.template load<true>(Vh, Nk, j, 64, vs(buf));
   };
 
   f32x16 dqacc[T::DB];
@@ -435,25 +493,26 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   if (n_kt > 0) {
     stage_direct(0, 0);
-    st.load(krs, krs, 0, 0, 0, tid);
-    st.store(ks(0), kts(0), 0, tid);
+    st.load(Kh, Nk, 0);
+    st.store(kts(0), tid);
     wait_vmem();
     __syncthreads();
   }
+  wait_vmem();  // Q^T, dO^T and the row statistics, on every path into the sweep
   auto step = [&](auto masked, int j) {
     constexpr bool MASKED = decltype(masked)::value;
     const int cur = j & 1;
     const bool more = j + 1 < n_kt;
     if (more) {
       stage_direct(j + 1, cur ^ 1);
-      st.load(krs, krs, j + 1, j + 1, 0, tid);
+      st.load(Kh, Nk, j + 1);
     }
     f32x16 sacc[2], dpacc[2];
     score_tile<D>(ks(cur), qf, ko, sacc);
     score_tile<D>(vs(cur), dof, ko, dpacc);
     u32x4 pw[4];
     dq_scores_to_ds<MASKED, D>(sacc, dpacc, c, lse2, drow, j * 64, kmax, h, pw);
-    if (more) st.store(ks(cur ^ 1), kts(cur ^ 1), 0, tid);
+    if (more) st.store(kts(cur ^ 1), tid);
     pv_tile<D>(kts(cur), pw, vo, dqacc);  // dQ^T += K^T dS^T
     wait_vmem();
     __syncthreads();

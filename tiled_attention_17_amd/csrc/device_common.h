@@ -84,9 +84,34 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, i
                                            0, 0, 0);
 }
 
+// The same transfer issued through inline assembly, which the compiler
+// does not see as a write to LDS. For the intrinsic above it conservatively
+// waits for the transfer before any later LDS read of the workgroup's
+// memory, which exposes the whole latency of a tile staged for the next
+// step at the start of the current one; with this form the caller alone
+// orders the transfer, by wait_vmem() before the barrier that publishes the
+// tile (vector-memory loads complete in order, so the compiler's own counted
+// waits for other loads stay correct).
+__device__ __forceinline__ void lds_dma16_async(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
+  const unsigned m = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(m)), "v"(voff), "s"(r)
+      : "memory", "m0");
+}
+
 // Waits until this wave's vector-memory operations are done (among them the
 // buffer_load ... lds writes of a directly staged tile).
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// (The builtin rather than inline assembly, so that the compiler's own wait
+// insertion knows every earlier load has completed here: a wait it cannot
+// see leaves loads it believes pending, and on a later path it would wait
+// for them again, counting the tile staged meanwhile as well.)
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left at their maximum
+}
 
 // 8 bf16 from two transposed 4-element LDS reads (see the header comment).
 __device__ __forceinline__ bf16x8 lds_read_tr_pair(const bf16* p0, const bf16* p1) {

@@ -293,14 +293,18 @@ struct KDirect {
     }
   }
   // Tile `tile` (rows tile * bn ..) of a head whose K rows start at kbase
-  // and number n_rows.
+  // and number n_rows. ASYNC issues the transfers with lds_dma16_async.
+  template <bool ASYNC = false>
   __device__ __forceinline__ void load(const bf16* kbase, int n_rows, int tile, int bn, bf16* kt) const {
     const int row0 = tile * bn;
     const int rem = n_rows > row0 ? n_rows - row0 : 0;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kbase + (size_t)row0 * D), 0, rem * D * 2, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lds_dma16(r, kt + (lds_row0 + i * RPI) * D, voff[i]);
+    for (int i = 0; i < NI; ++i) {
+      if (ASYNC) lds_dma16_async(r, kt + (lds_row0 + i * RPI) * D, voff[i]);
+      else lds_dma16(r, kt + (lds_row0 + i * RPI) * D, voff[i]);
+    }
   }
 };
 
