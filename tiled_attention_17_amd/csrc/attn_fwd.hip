@@ -353,7 +353,7 @@ void attn_fwd_bf16_kernel(const FwdParams p) {
     const int cur = j & 1;
     const bool more = j + 1 < n_kt;
     if (more) {
-      kd.load(Kh, p.Nk, t0 + j + 1, 64, ks(cur ^ 1));
+      kd.template load<true>(Kh, p.Nk, t0 + j + 1, 64, ks(cur ^ 1));
       st.load(krs, vrs, t0 + j + 1, t0 + j + 1, 0, tid);
     }
     f32x16 sacc[2];
@@ -457,7 +457,7 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
     const int cur = i & 1;
     const bool more = i + 1 < my_n;
     if (more) {
-      kd.load(Kh, p.Nk, t0 + i + 1, 64, ks(cur ^ 1));
+      kd.template load<true>(Kh, p.Nk, t0 + i + 1, 64, ks(cur ^ 1));
       st.load(krs, vrs, t0 + i + 1, t0 + i + 1, 0, gtid);
     }
     f32x16 sacc[2];

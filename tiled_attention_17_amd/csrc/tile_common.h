@@ -228,14 +228,16 @@ struct Stager {
     }
     const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
     const int col = 8 * (r % T::CPR), g = r / T::CPR;
+    // Waves past the last pass load a valid pass again and store nothing: a
+    // load under a wave-uniform condition made the compiler merge the
+    // loaded registers with their old values right after the loads, and
+    // that merge waited for the loads (and everything issued before them).
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
-      const int pass = wave + i * WAVES;
-      if (VPASS % WAVES == 0 || pass < VPASS) {
-        const int kv = kt_v * T::BN + r0 + pass * T::VKEYS + 8 * g + 2 * p;
-        va[i] = buffer_load16(vr, (kv * D + col) * 2);
-        vb[i] = buffer_load16(vr, ((kv + 1) * D + col) * 2);
-      }
+      const int pass = VPASS % WAVES == 0 ? wave + i * WAVES : min(wave + i * WAVES, VPASS - 1);
+      const int kv = kt_v * T::BN + r0 + pass * T::VKEYS + 8 * g + 2 * p;
+      va[i] = buffer_load16(vr, (kv * D + col) * 2);
+      vb[i] = buffer_load16(vr, ((kv + 1) * D + col) * 2);
     }
   }
   __device__ __forceinline__ void store(bf16* kt, bf16* vt, int r0, int t) {
