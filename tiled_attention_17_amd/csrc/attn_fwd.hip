@@ -698,15 +698,35 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const FwdParams p) {
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // The next tile's K and V are loaded into registers while the current one
+  // is worked on, and written to LDS after the workgroup is done with it.
+  constexpr int EPT = C::BN * D / C::THREADS;  // elements of each tile per thread
+  float kn[EPT], vn[EPT];
+  auto load_tile = [&](int j) {
+    const int key0 = kr.k_begin + j * C::BN;
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int e = tid + r * C::THREADS, row = e / D, col = e % D, key = key0 + row;
+      const bool ok = key < p.Nk;
+      kn[r] = ok ? K[kbase + (size_t)key * D + col] : 0.f;
+      vn[r] = ok ? V[kbase + (size_t)key * D + col] : 0.f;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int e = tid + r * C::THREADS, row = e / D, col = e % D;
+      kt[row * C::KPITCH + col] = kn[r];
+      vt[row * C::VPITCH + col] = vn[r];
+    }
+  };
+  if (kr.n_tiles > 0) load_tile(0);
+
   for (int j = 0; j < kr.n_tiles; ++j) {
     const int key0 = kr.k_begin + j * C::BN;
-    for (int e = tid; e < C::BN * D; e += C::THREADS) {
-      const int row = e / D, col = e % D, key = key0 + row;
-      const bool ok = key < p.Nk;
-      kt[row * C::KPITCH + col] = ok ? K[kbase + (size_t)key * D + col] : 0.f;
-      vt[row * C::VPITCH + col] = ok ? V[kbase + (size_t)key * D + col] : 0.f;
-    }
+    store_tile();
     __syncthreads();
+    if (j + 1 < kr.n_tiles) load_tile(j + 1);
 
     f32x16 sacc;
 #pragma unroll
