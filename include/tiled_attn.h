@@ -96,12 +96,13 @@ const char* attn_last_error(void);
  * Source: Lecture 17 page §8.1 (definition), §8.2 (tiled, IO-aware flow),
  * §8.3 (online softmax update m' = max(m, max s), alpha = e^(m - m'),
  * l' = alpha l + sum p, o' = alpha o + p V, O = o / l).
- * The library picks the workgroup shape of the bf16 kernels from the grid
+ * The library picks the workgroup shape of the kernels from the grid
  * size; two environment variables override that choice (for tests and
  * experiments; results agree within the stated tolerance either way):
- * TILED_ATTN_FWD_WAVES = 2, 4 or 8 waves per workgroup, and
- * TILED_ATTN_FWD_KSPLIT = 1 (never) or 2 (where the launch allows it) for
- * splitting a workgroup's keys between two wave groups.
+ * TILED_ATTN_FWD_WAVES = 2, 4 or 8 waves per workgroup of the bf16 kernels,
+ * and TILED_ATTN_FWD_KSPLIT = 1 (never) or 2 (where the launch allows it)
+ * for splitting a workgroup's keys between its waves (bf16: two wave groups
+ * of an unmasked launch; fp32: the four waves of a 32-query workgroup).
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,

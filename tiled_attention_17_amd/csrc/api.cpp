@@ -126,7 +126,7 @@ int env_waves() {
 }
 
 // TILED_ATTN_FWD_KSPLIT=1 (never) or 2 (where allowed) overrides the
-// choice of splitting a workgroup's keys between two wave groups.
+// choice of splitting a workgroup's keys between its waves.
 int env_ksplit() {
   const char* s = std::getenv("TILED_ATTN_FWD_KSPLIT");
   if (!s) return 0;

@@ -656,6 +656,29 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // fp32 forward (fp32 storage and arithmetic; v_mfma_f32_32x32x2_f32)
 // ---------------------------------------------------------------------------
+// Buffer resource over rows [row0, min(row0 + rows, n)) of a row-major
+// fp32 [n, D] matrix: loads at or past the last of those rows return zeros
+// without touching memory (no branch, and so no wait where paths would
+// join). With row0 >= n the range is empty.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rows_rsrc(const float* base, int row0, int rows,
+                                                                int n) {
+  const int cnt = max(0, min(rows, n - row0));
+  // The arguments are wave-uniform, but the compiler cannot always tell;
+  // without these it puts every load in a loop over the distinct values.
+  const uintptr_t a = (uintptr_t)(base + (size_t)row0 * D);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uintptr_t)hi << 32) | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(cnt * D * 4), kBufferRsrcWord3);
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ f32x4 buffer_load_f32x4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 template <int D>
 struct FwdF32Cfg {
   static constexpr int NW = 4;
@@ -687,9 +710,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const FwdParams p) {
   const int kmax = row_kmax(p, kr, q_row);
 
   float qf[C::DK];  // lane (query lq, half h) holds Q[q][2 s + h]
-  const float* qrow = (const float*)p.q + ((size_t)ti.bh * p.Nq + q_row) * D;
+  const __amdgpu_buffer_rsrc_t qr = f32_rows_rsrc<D>((const float*)p.q + (size_t)ti.bh * p.Nq * D,
+                                                     ti.qt * C::BM + wave * C::R, C::R, p.Nq);
 #pragma unroll
-  for (int s = 0; s < C::DK; ++s) qf[s] = q_ok ? qrow[2 * s + h] : 0.f;
+  for (int s = 0; s < C::DK; ++s) qf[s] = buffer_load_f32(qr, 4 * (lq * D + 2 * s + h));
 
   f32x16 oacc[C::DB];
 #pragma unroll
@@ -704,12 +728,13 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const FwdParams p) {
   float kn[EPT], vn[EPT];
   auto load_tile = [&](int j) {
     const int key0 = kr.k_begin + j * C::BN;
+    const __amdgpu_buffer_rsrc_t kr_ = f32_rows_rsrc<D>(K + kbase, key0, C::BN, p.Nk);
+    const __amdgpu_buffer_rsrc_t vr_ = f32_rows_rsrc<D>(V + kbase, key0, C::BN, p.Nk);
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {
-      const int e = tid + r * C::THREADS, row = e / D, col = e % D, key = key0 + row;
-      const bool ok = key < p.Nk;
-      kn[r] = ok ? K[kbase + (size_t)key * D + col] : 0.f;
-      vn[r] = ok ? V[kbase + (size_t)key * D + col] : 0.f;
+      const int e = tid + r * C::THREADS;  // element e of the tile: row e / D, column e % D
+      kn[r] = buffer_load_f32(kr_, 4 * e);
+      vn[r] = buffer_load_f32(vr_, 4 * e);
     }
   };
   auto store_tile = [&]() {
@@ -790,6 +815,206 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const FwdParams p) {
         *(f32x4*)(orow + 32 * db + 8 * r + 4 * h) = w;
       }
     if (h == 0) (part ? p.lse_part : p.lse)[row] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward, keys split inside the workgroup: NG waves take the same 32
+// queries, wave g every NG-th key tile (g, g + NG, ...), and at the end
+// waves 1 .. NG-1 hand their running (m, l, o) to wave 0 through LDS, which
+// merges them by the online update's rule (Lecture 17 page §8.3). Both
+// operands that vary with the keys come straight from memory into registers
+// (the next tile's while the current one is worked on), so the loop has no
+// LDS traffic and no workgroup barrier. For small grids (few heads, short
+// sequences): there 128-query workgroups keep only a few SIMDs busy, each
+// with a long serial chain of fp32 MFMAs.
+// ---------------------------------------------------------------------------
+template <int D>
+struct FwdF32SplitCfg {
+  // Waves (key groups) per workgroup: one per SIMD, so that each has the
+  // registers for its current and next tile's operands. A compute unit's
+  // fp32 matrix rate is what it is, so more waves would not make one
+  // workgroup finish sooner.
+  static constexpr int NG = 4;
+  static constexpr int BM = 32;
+  static constexpr int BN = 32;
+  static constexpr int DH = D / 2;        // d-values per lane half of the score operands
+  static constexpr int DB = D / 32;
+  static constexpr int NV = 16 * DB;      // V^T operand values per lane and tile
+  static constexpr int NE = 16 * DB + 2;  // floats one lane hands over: o, m, l
+};
+
+template <int D>
+__global__ __launch_bounds__(FwdF32SplitCfg<D>::NG * 64) void attn_fwd_f32_ksplit_kernel(
+    const FwdParams p) {
+  using C = FwdF32SplitCfg<D>;
+  __shared__ float xch[(C::NG - 1) * C::NE * 64];
+
+  const TileId ti = decode_tile(p);
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q_row = ti.qt * C::BM + lq;
+  const bool q_ok = q_row < p.Nq;
+  const KeyRange kr = key_range<C::BN>(p, ti.split, ti.qt * C::BM, C::BM);
+  const int kmax = row_kmax(p, kr, q_row);
+  const float* Kh = (const float*)p.k + (size_t)ti.bh * p.Nk * D;
+  const float* Vh = (const float*)p.v + (size_t)ti.bh * p.Nk * D;
+
+  // Score operands: step s of lane half h contracts d = h D/2 + s. Any
+  // assignment of d to the steps gives the same dot product; this one makes
+  // each lane's share of a Q or K row contiguous (16-byte loads).
+  float qf[C::DH];
+  {
+    const __amdgpu_buffer_rsrc_t qr = f32_rows_rsrc<D>((const float*)p.q + (size_t)ti.bh * p.Nq * D,
+                                                       ti.qt * C::BM, C::BM, p.Nq);
+#pragma unroll
+    for (int c = 0; c < C::DH / 4; ++c) {
+      const f32x4 x = buffer_load_f32x4(qr, 4 * (lq * D + h * C::DH + 4 * c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * c + e] = x[e];
+    }
+  }
+
+  // Tile j: K rows as the A operand of S^T = K Q^T (lane: key lq, its d-half
+  // h), V^T as the A operand of O^T += V^T P^T (lane: d = 32 db + lq; step s
+  // takes key 8 (s/4) + 4 h + s%4, the key of accumulator slot s of S^T).
+  // Rows past N_k read as zero.
+  auto load_tile = [&](int j, float* kd, float* vd) {
+    const int key0 = kr.k_begin + j * C::BN;
+    const __amdgpu_buffer_rsrc_t kr_ = f32_rows_rsrc<D>(Kh, key0, C::BN, p.Nk);
+    const __amdgpu_buffer_rsrc_t vr_ = f32_rows_rsrc<D>(Vh, key0, C::BN, p.Nk);
+#pragma unroll
+    for (int c = 0; c < C::DH / 4; ++c) {
+      const f32x4 x = buffer_load_f32x4(kr_, 4 * (lq * D + h * C::DH + 4 * c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kd[4 * c + e] = x[e];
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        vd[s * C::DB + db] = buffer_load_f32(vr_, 4 * ((8 * (s >> 2) + 4 * h + (s & 3)) * D + 32 * db + lq));
+  };
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int n_mine = kr.n_tiles > g ? (kr.n_tiles - g + C::NG - 1) / C::NG : 0;
+  float kn[C::DH], vn[C::NV];
+  if (n_mine > 0) load_tile(g, kn, vn);
+  for (int i = 0; i < n_mine; ++i) {
+    const int j = g + C::NG * i;
+    const int key0 = kr.k_begin + j * C::BN;
+    float kc[C::DH], vc[C::NV];
+#pragma unroll
+    for (int e = 0; e < C::DH; ++e) kc[e] = kn[e];
+#pragma unroll
+    for (int e = 0; e < C::NV; ++e) vc[e] = vn[e];
+    // Unconditional (the last step reloads its own tile): a load under a
+    // branch would make the compiler wait for it where the paths join.
+    load_tile(i + 1 < n_mine ? j + C::NG : j, kn, vn);
+
+    // Two independent accumulation chains over d, added at the end.
+    f32x16 sa, sb;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sa[e] = sb[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::DH; s += 2) {
+      sa = mfma32x32x2f32(kc[s], qf[s], sa);
+      sb = mfma32x32x2f32(kc[s + 1], qf[s + 1], sb);
+    }
+    float sv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sv[e] = sa[e] + sb[e];
+
+    // key of slot e: key0 + 8 (e/4) + 4 h + e%4; keys past kmax are dropped
+    const bool masked = j >= kr.n_full;
+    if (masked) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (key0 + 8 * (e >> 2) + 4 * h + (e & 3) > kmax) sv[e] = -INFINITY;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+    mx = max_with_other_half(mx);
+    // A row with no visible key so far keeps m = -inf, l = 0, o = 0.
+    const float mt = mx == -INFINITY ? -INFINITY : mx * p.c;
+    const float m_new = fmaxf(m_run, mt);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    float pr[16], lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      pr[e] = fast_exp2(fmaf(sv[e], p.c, -m_ref));
+      if (masked && sv[e] == -INFINITY) pr[e] = 0.f;
+      lsum += pr[e];
+    }
+    l_run = fmaf(alpha, l_run, lsum);
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] = mfma32x32x2f32(vc[s * C::DB + db], pr[s], oacc[db]);
+  }
+
+  // Hand-over ([wave - 1][element][lane]) and merge in wave 0:
+  // m = max_g m_g, l = sum_g 2^(m_g - m) l_g, o likewise.
+  float* xb = xch + lane;
+  if (g > 0) {
+    float* w = xb + (size_t)(g - 1) * C::NE * 64;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w[(16 * db + e) * 64] = oacc[db][e];
+    w[(C::NE - 2) * 64] = m_run;
+    w[(C::NE - 1) * 64] = l_run;
+  }
+  __syncthreads();
+  if (g > 0) return;
+  float m = m_run;
+  for (int k = 0; k < C::NG - 1; ++k) m = fmaxf(m, xb[(k * C::NE + C::NE - 2) * 64]);
+  const float m_ref = m == -INFINITY ? 0.f : m;  // no group saw a visible key
+  const float a0 = fast_exp2(m_run - m_ref);
+  float l = a0 * l_run;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] *= a0;
+  for (int k = 0; k < C::NG - 1; ++k) {
+    const float* r = xb + (size_t)k * C::NE * 64;
+    const float a = fast_exp2(r[(C::NE - 2) * 64] - m_ref);
+    l = fmaf(a, r[(C::NE - 1) * 64], l);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] = fmaf(a, r[(16 * db + e) * 64], oacc[db][e]);
+  }
+
+  const float l_tot = add_other_half(l);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_ok) {
+    const bool part = p.n_splits > 1;
+    const size_t row = part ? ((size_t)ti.split * p.BH + ti.bh) * p.Nq + q_row
+                            : (size_t)ti.bh * p.Nq + q_row;
+    float* orow = (part ? p.o_part : (float*)p.o) + row * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 w = {oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv, oacc[db][4 * r + 2] * inv,
+                   oacc[db][4 * r + 3] * inv};
+        *(f32x4*)(orow + 32 * db + 8 * r + 4 * h) = w;
+      }
+    if (h == 0) (part ? p.lse_part : p.lse)[row] = (m + fast_log2(l_tot)) * kLn2;
   }
 }
 
@@ -909,10 +1134,24 @@ static bool use_ksplit(const FwdArgs& a, int64_t splits, int nw) {
 }
 
 template <int D>
-static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total) {
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)total), dim3(FwdF32Cfg<D>::THREADS), 0,
-                     (hipStream_t)a.stream, p);
+static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total, bool ksplit) {
+  if (ksplit)
+    hipLaunchKernelGGL((attn_fwd_f32_ksplit_kernel<D>), dim3((unsigned)total),
+                       dim3(FwdF32SplitCfg<D>::NG * 64), 0, (hipStream_t)a.stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)total), dim3(FwdF32Cfg<D>::THREADS), 0,
+                       (hipStream_t)a.stream, p);
   return hipGetLastError();
+}
+
+// fp32: split each workgroup's keys between its waves (32 queries per
+// workgroup) when 128-query workgroups would not cover every compute unit.
+static bool use_f32_ksplit(const FwdArgs& a) {
+  if (a.ksplit == 1) return false;
+  if (a.ksplit == 2) return true;
+  const int64_t tiles = a.BH * ((a.Nq + FwdF32Cfg<64>::BM - 1) / FwdF32Cfg<64>::BM) *
+                        (a.n_splits > 1 ? a.n_splits : 1);
+  return tiles < (int64_t)a.num_cus;
 }
 
 // Workgroup size choice: the largest query tile whose grid (with the key
@@ -956,9 +1195,10 @@ int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) 
 hipError_t launch_attn_fwd(const FwdArgs& a) {
   int64_t total = 0;
   if (a.dtype_fp32) {
-    const FwdParams p = make_params(a, FwdF32Cfg<64>::BM, &total);
+    const bool ks = use_f32_ksplit(a);
+    const FwdParams p = make_params(a, ks ? FwdF32SplitCfg<64>::BM : FwdF32Cfg<64>::BM, &total);
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipError_t e = a.d == 64 ? launch_f32<64>(a, p, total) : launch_f32<128>(a, p, total);
+    hipError_t e = a.d == 64 ? launch_f32<64>(a, p, total, ks) : launch_f32<128>(a, p, total, ks);
     if (e != hipSuccess || p.n_splits == 1) return e;
     return launch_attn_merge(p.o_part, p.lse_part, p.n_splits, a.BH * a.Nq, a.d, a.o, a.lse, true,
                              a.stream);

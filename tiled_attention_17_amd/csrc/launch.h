@@ -24,8 +24,9 @@ struct FwdArgs {
   void* stream;
   int num_cus;      // compute units of the device (grid sizing)
   int waves;        // 0 = choose; else waves per workgroup of the bf16 kernel (2, 4 or 8)
-  int ksplit;       // 0 = choose; 1 = never; 2 = split the keys between two wave groups of a
-                    // workgroup where the launch allows it (bf16, no mask, no key splits, waves < 8)
+  int ksplit;       // 0 = choose; 1 = never; 2 = split a workgroup's keys between its waves
+                    // where the launch allows it (bf16: two wave groups, no mask, no key splits,
+                    // waves < 8; fp32: always)
 };
 
 // Parameters of one forward kernel launch (kernel argument, by value).
