@@ -334,17 +334,14 @@ void attn_fwd_bf16_kernel(const FwdParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   const int n_kt = kr.n_tiles;
-  // The next tile's K goes straight to LDS; its V is staged through
-  // registers in two halves of 32 rows (the first half's loads overlap the
-  // score product and softmax, the second half's the value product).
+  // The next tile's K goes straight to LDS and its whole V into registers
+  // at the start of a step; V is transposed into LDS after the step's value
+  // product, so its loads have the whole step to arrive.
   const KDirect<D, 64, NW> kd(0, wave, lane);
-  Stager<D, 32, NW * 64, 64, false> st;
+  Stager<D, 64, NW * 64, 64, false> st;
   kd.load(Kh, p.Nk, t0, 64, ks(0));
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    st.load(krs, vrs, t0, t0, 32 * half, tid);
-    st.store(ks(0), vs(0), 32 * half, tid);
-  }
+  st.load(krs, vrs, t0, t0, 0, tid);
+  st.store(ks(0), vs(0), 0, tid);
   wait_vmem();
   __syncthreads();
 
@@ -360,12 +357,8 @@ void attn_fwd_bf16_kernel(const FwdParams p) {
     u32x4 pw[4];
     score_tile<D>(ks(cur), qf, ko, sacc);
     softmax_tile<MASKED, T::DB>(sacc, p.c, kr.k_begin + j * T::BN, kmax, h, m_run, l_run, oacc, pw);
-    if (more) {
-      st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
-      st.load(krs, vrs, t0 + j + 1, t0 + j + 1, 32, tid);
-    }
     pv_tile<D>(vs(cur), pw, vo, oacc);
-    if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 32, tid);
+    if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
     wait_vmem();  // K tile written to LDS
     __syncthreads();
   };
@@ -438,15 +431,15 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // The next tile's K goes straight to LDS and its whole V into registers
+  // at the start of a step; V is transposed into LDS after the step's value
+  // product, so its loads have the whole step to arrive.
   const KDirect<D, 64, NW> kd(0, wave, lane);
-  Stager<D, 32, NW * 64, 64, false> st;
+  Stager<D, 64, NW * 64, 64, false> st;
   if (my_n > 0) {
     kd.load(Kh, p.Nk, t0, 64, ks(0));
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      st.load(krs, vrs, t0, t0, 32 * half, gtid);
-      st.store(ks(0), vs(0), 32 * half, gtid);
-    }
+    st.load(krs, vrs, t0, t0, 0, gtid);
+    st.store(ks(0), vs(0), 0, gtid);
   }
   wait_vmem();
   __syncthreads();
@@ -465,12 +458,8 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
     score_tile<D>(ks(cur), qf, ko, sacc);
     softmax_tile<MASKED, T::DB>(sacc, p.c, kr.k_begin + (my_first + i) * T::BN, kmax, h, m_run, l_run,
                                 oacc, pw);
-    if (more) {
-      st.store(ks(cur ^ 1), vs(cur ^ 1), 0, gtid);
-      st.load(krs, vrs, t0 + i + 1, t0 + i + 1, 32, gtid);
-    }
     pv_tile<D>(vs(cur), pw, vo, oacc);
-    if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 32, gtid);
+    if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 0, gtid);
     wait_vmem();  // K tile written to LDS
     __syncthreads();
   };
