@@ -102,7 +102,9 @@ const char* attn_last_error(void);
  * TILED_ATTN_FWD_WAVES = 2, 4 or 8 waves per workgroup of the bf16 kernels,
  * and TILED_ATTN_FWD_KSPLIT = 1 (never) or 2 (where the launch allows it)
  * for splitting a workgroup's keys between its waves (bf16: two wave groups
- * of an unmasked launch; fp32: the four waves of a 32-query workgroup).
+ * of an unmasked launch; fp32: the four waves of a 32-query workgroup);
+ * TILED_ATTN_FWD_DECODE = 1 keeps bf16 launches with one query per head on
+ * the tiled kernels instead of the one-query kernel.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,

@@ -236,6 +236,37 @@ def test_splits_match_single_pass_closely():
     _check(x, o4, l4, w.scale, False, BF16_TOL, BF16_REL)
 
 
+@pytest.mark.parametrize("decode", ["0", "1"])
+@pytest.mark.parametrize("splits", [1, 3, 0])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nk", [1, 7, 65, 300, 4096])
+def test_one_query_per_head(Nk, d, splits, decode, monkeypatch):
+    # N_q = 1 on the one-query kernel (0) and on the tiled kernels (1): a
+    # ragged last key block, fewer key blocks than waves (waves without a
+    # key), key splits given and chosen by the library.
+    monkeypatch.setenv("TILED_ATTN_FWD_DECODE", decode)
+    w = _wl(2, 3, 1, Nk, d, seed=700 + Nk + d, q_std=3.0)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL)
+
+
+@pytest.mark.parametrize("Nk", [1, 130, 2000])
+def test_one_query_per_head_causal_and_empty(Nk):
+    # With one query the causal window covers every key; and a head without
+    # keys gives O = 0, LSE = -inf.
+    w = _wl(3, 2, 1, Nk, 128, seed=710 + Nk)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, True, BF16_TOL, BF16_REL)
+    kv = torch.empty(3, 2, 0, 128, dtype=torch.bfloat16, device="cuda")
+    o0, l0 = ta.attn_fwd_ex(x["q"], kv, kv.clone())
+    torch.cuda.synchronize()
+    assert torch.all(o0 == 0) and torch.all(torch.isneginf(l0))
+
+
 def test_auto_splits_decode_shape():
     w = _wl(4, 8, 1, 3000, 128, seed=41)
     x = _cuda(make_inputs(w))

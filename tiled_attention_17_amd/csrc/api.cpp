@@ -134,6 +134,13 @@ int env_ksplit() {
   return (k == 1 || k == 2) ? k : 0;
 }
 
+// TILED_ATTN_FWD_DECODE=1 keeps bf16 launches with one query per head on
+// the tiled kernels instead of the one-query kernel.
+int env_decode() {
+  const char* s = std::getenv("TILED_ATTN_FWD_DECODE");
+  return (s && std::atoi(s) == 1) ? 1 : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,7 +222,7 @@ attn_status fwd_common(const void* q, const void* k, const void* v, void* o, flo
   if (cus == 0 && (s = device_cus(&cus)) != ATTN_OK) return s;
   tattn::FwdArgs a{q, k, v, o, lse, bh, Nq, Nk, d, scale, dtype == ATTN_FP32,
                    mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves(),
-                   env_ksplit()};
+                   env_ksplit(), env_decode()};
   const hipError_t he = tattn::launch_attn_fwd(a);
   if (he != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(he));
   return ok();

@@ -643,6 +643,170 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 forward for one query per head (decoding): a stream over K and V with
+// no matrix product worth the matrix cores (an MFMA tile would leave 31 of
+// its 32 query rows empty). Each key row is held by LPK = D / 8 lanes, 16
+// bytes each: the score is a v_dot2 over the lane's 8 d-values reduced over
+// its LPK lanes with DPP, and the lane's 8 output values take p * v. A wave
+// takes 64-key blocks wave, wave + WAVES, ... of the workgroup's key range
+// with all 2 * 64 * D * 2 bytes of a block's K and V loads in flight at
+// once, keeps the running (m, l, o) of the online update (Lecture 17 page
+// §8.3) per lane, and the waves merge theirs through LDS at the end.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DecodeCfg {
+  static constexpr int WAVES = 4;
+  static constexpr int LPK = D / 8;     // lanes per key row
+  static constexpr int KPI = 64 / LPK;  // keys per load instruction: 4 (d = 128) or 8 (d = 64)
+  static constexpr int KPB = 64;        // keys per wave and block
+  static constexpr int U = KPB / KPI;   // load instructions per tensor and block
+};
+
+// Sum over the LPK = 8 or 16 lanes of a row group (DPP within rows of 16).
+// Two packed bf16 from a 32-bit word. (A by-value argument on purpose:
+// __builtin_bit_cast applied directly to an element of a vector value, as in
+// bit_cast(T, v[j]), was compiled as a cast of element 0 for every j.)
+__device__ __forceinline__ bf16x2_ev as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2_ev, u); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int LPK>
+__device__ __forceinline__ float sum_lane_group(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_f32<0x141>(x);  // row_half_mirror: the other quad of each 8 lanes
+  if (LPK == 16) x += dpp_f32<0x140>(x);  // row_mirror: the other half of each 16 lanes
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_bf16_decode_kernel(const FwdParams p) {
+  using C = DecodeCfg<D>;
+  __shared__ float xch[C::WAVES][D + 2];  // per wave: o, m, l
+
+  const TileId ti = decode_tile(p);  // one query tile (N_q = 1)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ch = lane % C::LPK, kg = lane / C::LPK;  // d-chunk of the lane, key within a load
+  const KeyRange kr = key_range<C::KPB>(p, ti.split, 0, 1);
+  const int k_lim = row_kmax(p, kr, 0) + 1;  // first key past what the query sees
+  const bf16* Kh = (const bf16*)p.k + (size_t)ti.bh * p.Nk * D;
+  const bf16* Vh = (const bf16*)p.v + (size_t)ti.bh * p.Nk * D;
+  const u32x4 qv = *(const u32x4*)((const bf16*)p.q + (size_t)ti.bh * D + 8 * ch);
+
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // l_run: this lane's key group only
+
+  for (int b = wave; b < kr.n_tiles; b += C::WAVES) {
+    const int key0 = kr.k_begin + b * C::KPB;
+    // Rows past N_k read as zero (range-checked resources over this block).
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(C::KPB, p.Nk - key0)));
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + (size_t)key0 * D), 0, rows * D * 2, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vh + (size_t)key0 * D), 0, rows * D * 2, kBufferRsrcWord3);
+    u32x4 kk[C::U], vv[C::U];
+#pragma unroll
+    for (int i = 0; i < C::U; ++i) kk[i] = buffer_load16(krs, ((i * C::KPI + kg) * D + 8 * ch) * 2);
+#pragma unroll
+    for (int i = 0; i < C::U; ++i) vv[i] = buffer_load16(vrs, ((i * C::KPI + kg) * D + 8 * ch) * 2);
+
+    // Scores in the exp2 domain (c = scale log2 e); keys the query does not
+    // see (past the split's range or the causal window) get -inf.
+    float sc[C::U], bmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < C::U; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kk[i][j]), as_bf16x2(qv[j]), a, false);
+      a = sum_lane_group<C::LPK>(a) * p.c;
+      sc[i] = key0 + i * C::KPI + kg < k_lim ? a : -INFINITY;
+      bmax = fmaxf(bmax, sc[i]);
+    }
+    // Block maximum over the wave's key groups (lanes ^ LPK .. ^ 32).
+#pragma unroll
+    for (int x = C::LPK; x < 32; x *= 2) bmax = fmaxf(bmax, __shfl_xor(bmax, x, 64));
+    bmax = max_with_other_half(bmax);
+    const float m_new = fmaxf(m_run, bmax);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < C::U; ++i) {
+      const float pr = fast_exp2(sc[i] - m_ref);  // 0 for a key the query does not see
+      l_run += pr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = fmaf(pr, __uint_as_float(vv[i][j] << 16), o[2 * j]);
+        o[2 * j + 1] = fmaf(pr, __uint_as_float(vv[i][j] & 0xFFFF0000u), o[2 * j + 1]);
+      }
+    }
+  }
+
+  // Sum l and o over the wave's key groups; every lane then holds the
+  // wave's totals for its d-chunk.
+#pragma unroll
+  for (int x = C::LPK; x < 32; x *= 2) {
+    l_run += __shfl_xor(l_run, x, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], x, 64);
+  }
+  l_run = add_other_half(l_run);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = add_other_half(o[e]);
+  if (kg == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xch[wave][8 * ch + e] = o[e];
+    if (ch == 0) {
+      xch[wave][D] = m_run;
+      xch[wave][D + 1] = l_run;
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || kg != 0) return;
+
+  // Merge of the waves: m = max m_w, l = sum 2^(m_w - m) l_w, o likewise.
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < C::WAVES; ++w) m = fmaxf(m, xch[w][D]);
+  const float m_ref = m == -INFINITY ? 0.f : m;  // no wave saw a visible key
+  float l = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < C::WAVES; ++w) {
+    const float a = fast_exp2(xch[w][D] - m_ref);
+    l = fmaf(a, xch[w][D + 1], l);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(a, xch[w][8 * ch + e], acc[e]);
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse = (m + fast_log2(l)) * kLn2;  // -inf for a row without keys
+  if (p.n_splits > 1) {
+    const size_t row = (size_t)ti.split * p.BH + ti.bh;
+    f32x4 w0 = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    f32x4 w1 = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    *(f32x4*)(p.o_part + row * D + 8 * ch) = w0;
+    *(f32x4*)(p.o_part + row * D + 8 * ch + 4) = w1;
+    if (ch == 0) p.lse_part[row] = lse;
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+    *(u32x4*)((bf16*)p.o + (size_t)ti.bh * D + 8 * ch) = w;
+    if (ch == 0) p.lse[ti.bh] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 forward (fp32 storage and arithmetic; v_mfma_f32_32x32x2_f32)
 // ---------------------------------------------------------------------------
 // Buffer resource over rows [row0, min(row0 + rows, n)) of a row-major
@@ -1105,6 +1269,13 @@ static hipError_t launch_bf16(const FwdArgs& a, const FwdParams& p, int64_t tota
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_bf16_decode(const FwdArgs& a, const FwdParams& p, int64_t total) {
+  hipLaunchKernelGGL((attn_fwd_bf16_decode_kernel<D>), dim3((unsigned)total), dim3(DecodeCfg<D>::WAVES * 64), 0,
+                     (hipStream_t)a.stream, p);
+  return hipGetLastError();
+}
+
 template <int D, int NW>
 static hipError_t launch_bf16_ksplit(const FwdArgs& a, const FwdParams& p, int64_t total) {
   hipLaunchKernelGGL((attn_fwd_bf16_ksplit_kernel<D, NW>), dim3((unsigned)total), dim3(2 * NW * 64), 0,
@@ -1169,6 +1340,13 @@ int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) 
     if (s < 2) return 1;
     return (int)(s < kMaxSplits ? s : kMaxSplits);
   };
+  if (!fp32 && Nq == 1) {
+    // One query per head (the one-query kernel): about one workgroup per
+    // compute unit, each split at least four 128-key tiles. More and
+    // shorter streams measured slower on the decode workload (2 splits:
+    // 5.8 TB/s, 4: 5.1 TB/s), and the merge is a launch of its own.
+    return clamp_splits((num_cus + BH - 1) / BH, 4);
+  }
   if (!fp32 && Nq >= 128) {
     const int64_t t8 = BH * ((Nq + 255) / 256);
     if (t8 >= num_cus) return 1;
@@ -1195,6 +1373,14 @@ hipError_t launch_attn_fwd(const FwdArgs& a) {
   const int64_t splits = a.n_splits > 1 ? (a.Nk + split_keys_for(a.Nk, a.n_splits) - 1) /
                                                split_keys_for(a.Nk, a.n_splits)
                                          : 1;
+  if (a.Nq == 1 && a.decode != 1) {
+    const FwdParams p = make_params(a, 1, &total);
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    hipError_t e = a.d == 64 ? launch_bf16_decode<64>(a, p, total) : launch_bf16_decode<128>(a, p, total);
+    if (e != hipSuccess || p.n_splits == 1) return e;
+    return launch_attn_merge(p.o_part, p.lse_part, p.n_splits, a.BH * a.Nq, a.d, a.o, a.lse, false,
+                             a.stream);
+  }
   const int nw = a.waves ? a.waves : fwd_bf16_waves(a.BH, a.Nq, splits, a.num_cus);
   const FwdParams p = make_params(a, 32 * nw, &total);
   if (total > INT32_MAX) return hipErrorInvalidValue;

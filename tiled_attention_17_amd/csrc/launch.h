@@ -27,6 +27,7 @@ struct FwdArgs {
   int ksplit;       // 0 = choose; 1 = never; 2 = split a workgroup's keys between its waves
                     // where the launch allows it (bf16: two wave groups, no mask, no key splits,
                     // waves < 8; fp32: always)
+  int decode;       // 0 = choose; 1 = never use the one-query kernel for N_q = 1 (bf16)
 };
 
 // Parameters of one forward kernel launch (kernel argument, by value).
