@@ -385,8 +385,10 @@ void attn_fwd_bf16_kernel(const FwdParams p) {
 // without a second launch. Unmasked launches only: the ragged end of the
 // key range is the only masked tile, and it is group 1's last.
 // ---------------------------------------------------------------------------
+// At D = 128 the four tile stages take 128 KiB of LDS, so one workgroup fits
+// on a compute unit: with NW = 2 that is one wave per SIMD.
 template <int D, int NW>
-__global__ __launch_bounds__(2 * NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(2 * NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 && NW == 2 ? 1 : 2, 2)))
 void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
   using T = FwdTile<D>;
   constexpr int BM = 32 * NW;

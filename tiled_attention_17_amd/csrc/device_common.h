@@ -92,15 +92,17 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, i
 // orders the transfer, by wait_vmem() before the barrier that publishes the
 // tile (vector-memory loads complete in order, so the compiler's own counted
 // waits for other loads stay correct).
+// The LDS address goes in as an m0 operand, so the compiler writes m0 itself
+// and knows its value afterwards (the s_nop keeps a wait state between that
+// write and the transfer that reads it).
 __device__ __forceinline__ void lds_dma16_async(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
   const unsigned m = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
-      : "s"(__builtin_amdgcn_readfirstlane(m)), "v"(voff), "s"(r)
-      : "memory", "m0");
+      : "v"(voff), "s"(r), "{m0}"(__builtin_amdgcn_readfirstlane(m))
+      : "memory");
 }
 
 // Waits until this wave's vector-memory operations are done (among them the
