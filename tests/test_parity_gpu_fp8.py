@@ -64,6 +64,20 @@ def test_quantize_rows_and_columns_bit_exact(shape, std):
     np.testing.assert_array_equal(st.cpu().numpy(), rst)
 
 
+@pytest.mark.parametrize("shape", [(2, 64, 37), (1, 160, 5), (1, 288, 200), (3, 32, 130)])
+def test_quantize_transposed_ragged_columns_bit_exact(shape):
+    # the transposed copy needs rows % 32 == 0 only: column counts that are not
+    # a multiple of 8 (element loads) or of the 64-column tile (partial tiles)
+    x = _bf16(shape, seed=shape[1] * 7 + shape[2], std=3.0)
+    x[0, 32:64, 0] = 0.0                     # an all-zero block of column 0 (where rows allow)
+    xg = x.cuda()
+    qt, st = ta.attn_quantize_mxfp8(xg, transpose=True)
+    torch.cuda.synchronize()
+    rqt, rst = mx_quantize(np.swapaxes(x.double().numpy(), -1, -2), axis=-1)
+    np.testing.assert_array_equal(qt.cpu().numpy(), rqt)
+    np.testing.assert_array_equal(st.cpu().numpy(), rst)
+
+
 def test_quantize_empty_is_noop():
     q, s = ta.attn_quantize_mxfp8(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
     assert q.shape == (0, 64) and s.shape == (0, 2)

@@ -104,32 +104,47 @@ __global__ __launch_bounds__(256) void mx_quantize_rows_kernel(const bf16* __res
 // Column-blocked and transposed: x [batch, rows, cols] bf16 (rows % 32 == 0)
 // -> q [batch, cols, rows] E4M3 (q[c][r] = x[r][c] scaled) and
 // sc [batch, cols, rows / 32]: each 32-row block of a column shares a scale.
-// A workgroup takes 32 rows x 256 columns through LDS; thread t then owns
-// column t of the tile.
+// A workgroup takes a tile of TR = 128 rows x TC = 64 columns through LDS
+// (16-byte loads, 8 threads per 128-byte row segment, when cols % 8 == 0;
+// element loads otherwise). Thread t then owns
+// column t / 4 and its 32-row block t % 4, so four adjacent threads write
+// one 128-byte run of a q row.
+constexpr int kQtTR = 128, kQtTC = 64;
 __global__ __launch_bounds__(256) void mx_quantize_cols_t_kernel(const bf16* __restrict__ x,
                                                                  uint8_t* __restrict__ q,
                                                                  uint8_t* __restrict__ sc, int rows,
-                                                                 int cols, int col_tiles) {
-  constexpr int TC = 256, PITCH = TC + 2;
-  __shared__ bf16 tile[32 * PITCH];
-  const int per_batch = (rows / 32) * col_tiles;
+                                                                 int cols, int row_tiles, int col_tiles) {
+  constexpr int TR = kQtTR, TC = kQtTC, PITCH = TC + 8;  // 144-byte LDS rows, 16-byte aligned
+  __shared__ __attribute__((aligned(16))) bf16 tile[TR * PITCH];
+  const int per_batch = row_tiles * col_tiles;
   const int batch = blockIdx.x / per_batch;
   const int rem = blockIdx.x - batch * per_batch;
-  const int rb = rem / col_tiles, ct = rem - rb * col_tiles;
-  const int r0 = rb * 32, c0 = ct * TC;
+  const int rt = rem / col_tiles, ct = rem - rt * col_tiles;
+  const int r0 = rt * TR, c0 = ct * TC;
   const bf16* xb = x + (size_t)batch * rows * cols;
-  for (int e = threadIdx.x; e < 32 * TC; e += 256) {
-    const int r = e / TC, c = e % TC;
-    tile[r * PITCH + c] = c0 + c < cols ? xb[(size_t)(r0 + r) * cols + c0 + c] : (bf16)0.f;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int pass = 0; pass < TR * TC / (8 * 256); ++pass) {
+    const int r = pass * 32 + t / 8, cc = 8 * (t % 8);
+    const bf16* src = xb + (size_t)(r0 + r) * cols + c0 + cc;
+    if (cols % 8 == 0) {  // 16-byte aligned row segments
+      u32x4 w = {0, 0, 0, 0};
+      if (r0 + r < rows && c0 + cc < cols) w = *(const u32x4*)src;
+      *(u32x4*)(tile + r * PITCH + cc) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        tile[r * PITCH + cc + e] = (r0 + r < rows && c0 + cc + e < cols) ? src[e] : (bf16)0.f;
+    }
   }
   __syncthreads();
-  const int c = c0 + threadIdx.x;
-  if (c >= cols) return;
+  const int c = t / 4, blk = t % 4;
+  if (c0 + c >= cols || r0 + 32 * blk >= rows) return;
   float v[32];
   float amax = 0.f;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    v[r] = (float)tile[r * PITCH + threadIdx.x];
+    v[r] = (float)tile[(32 * blk + r) * PITCH + c];
     amax = fmaxf(amax, fabsf(v[r]));
   }
   const unsigned code = mx_scale_code(__float_as_uint(amax));
@@ -138,10 +153,10 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_t_kernel(const bf16* __r
 #pragma unroll
   for (int w = 0; w < 8; ++w)
     o[w / 4][w % 4] = pack_e4m3x4(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv, v[4 * w + 3] * inv);
-  uint8_t* qrow = q + ((size_t)batch * cols + c) * rows + r0;
+  uint8_t* qrow = q + ((size_t)batch * cols + c0 + c) * rows + r0 + 32 * blk;
   ((u32x4*)qrow)[0] = o[0];
   ((u32x4*)qrow)[1] = o[1];
-  sc[((size_t)batch * cols + c) * (rows / 32) + rb] = (uint8_t)code;
+  sc[((size_t)batch * cols + c0 + c) * (rows / 32) + r0 / 32 + blk] = (uint8_t)code;
 }
 
 hipError_t launch_mx_quantize(const void* x, int64_t batch, int64_t rows, int64_t cols, bool transpose,
@@ -154,11 +169,12 @@ hipError_t launch_mx_quantize(const void* x, int64_t batch, int64_t rows, int64_
     hipLaunchKernelGGL(mx_quantize_rows_kernel, dim3((unsigned)wgs), dim3(256), 0, st, (const bf16*)x,
                        (uint8_t*)q, (uint8_t*)sc, blocks);
   } else {
-    const int64_t col_tiles = (cols + 255) / 256;
-    const int64_t wgs = batch * (rows / 32) * col_tiles;
+    const int64_t col_tiles = (cols + kQtTC - 1) / kQtTC;
+    const int64_t row_tiles = (rows + kQtTR - 1) / kQtTR;
+    const int64_t wgs = batch * row_tiles * col_tiles;
     if (wgs > INT32_MAX || rows > INT32_MAX || cols > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mx_quantize_cols_t_kernel, dim3((unsigned)wgs), dim3(256), 0, st, (const bf16*)x,
-                       (uint8_t*)q, (uint8_t*)sc, (int)rows, (int)cols, (int)col_tiles);
+                       (uint8_t*)q, (uint8_t*)sc, (int)rows, (int)cols, (int)row_tiles, (int)col_tiles);
   }
   return hipGetLastError();
 }
