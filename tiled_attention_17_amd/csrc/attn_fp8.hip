@@ -116,6 +116,10 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_t_kernel(const bf16* __r
                                                                  int cols, int row_tiles, int col_tiles) {
   constexpr int TR = kQtTR, TC = kQtTC, PITCH = TC + 8;  // 144-byte LDS rows, 16-byte aligned
   __shared__ __attribute__((aligned(16))) bf16 tile[TR * PITCH];
+  // Column c of row r sits at c ^ swz(r): the four threads reading one column
+  // (rows 32 apart, the same bank at this pitch) then hit four different
+  // 16-byte slots; a 16-byte group of 8 columns stays contiguous.
+  auto swz = [](int r) { return 8 * ((r >> 5) & 3); };
   const int per_batch = row_tiles * col_tiles;
   const int batch = blockIdx.x / per_batch;
   const int rem = blockIdx.x - batch * per_batch;
@@ -127,14 +131,14 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_t_kernel(const bf16* __r
   for (int pass = 0; pass < TR * TC / (8 * 256); ++pass) {
     const int r = pass * 32 + t / 8, cc = 8 * (t % 8);
     const bf16* src = xb + (size_t)(r0 + r) * cols + c0 + cc;
+    bf16* dst = tile + r * PITCH + (cc ^ swz(r));
     if (cols % 8 == 0) {  // 16-byte aligned row segments
       u32x4 w = {0, 0, 0, 0};
       if (r0 + r < rows && c0 + cc < cols) w = *(const u32x4*)src;
-      *(u32x4*)(tile + r * PITCH + cc) = w;
+      *(u32x4*)dst = w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        tile[r * PITCH + cc + e] = (r0 + r < rows && c0 + cc + e < cols) ? src[e] : (bf16)0.f;
+      for (int e = 0; e < 8; ++e) dst[e] = (r0 + r < rows && c0 + cc + e < cols) ? src[e] : (bf16)0.f;
     }
   }
   __syncthreads();
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_t_kernel(const bf16* __r
   float amax = 0.f;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    v[r] = (float)tile[(32 * blk + r) * PITCH + c];
+    v[r] = (float)tile[(32 * blk + r) * PITCH + (c ^ swz(32 * blk))];
     amax = fmaxf(amax, fabsf(v[r]));
   }
   const unsigned code = mx_scale_code(__float_as_uint(amax));
