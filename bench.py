@@ -6,10 +6,28 @@ workload: B=2, H=16, N=4096, d=128, bf16 Q, K, V ~ N(0,1), scale 1/sqrt(d),
 inputs resident in device memory before the timed region. Prints one JSON
 line with whole-job throughput (TFLOP/s at 4*B*H*N^2*d FLOPs per step), the
 roofline position of the kernel (timed live with HIP events on its launch
-stream), and the float64 CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+stream), the float64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores, and, in "extra", the other workloads' figures
+and the check of every measured output against the oracle.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Timing recipe (Lecture 17 page, §10.1-§10.2: warm up, time with events on the
+launch stream, repeat, verify the outputs):
+  * clock settle: under sustained load the MI355X raises its shader clock
+    over tens of milliseconds, so before the timed region each measurement
+    launches its kernel until --settle-ms of GPU time have passed (whatever
+    --warmup says), then --warmup more launches;
+  * every timed launch is bracketed by its own start and end events, so the
+    per-launch kernel time (mean, median, min) is reported beside the
+    whole-region step time;
+  * the short configurations (fp32 single head, d = 64) are also timed cold:
+    a 1 GiB scratch write between launches evicts the L2s and the Infinity
+    Cache, and each launch is timed on its own;
+  * the outputs of the timed launches are kept and compared with the oracle
+    in the CPU leg (whole heads of the headline workload, every head of the
+    d = 64 and fp32 workloads, sampled rows of the long sequence, sampled
+    heads of the backward).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T]
 """
 
 from __future__ import annotations
@@ -18,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -29,6 +48,7 @@ METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) + % of MI355X bf16 MFMA peak, 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_17_amd", "csrc", f)
                   for f in ("attn_fwd.hip", "tile_common.h", "device_common.h")]
+COLD_SCRATCH_BYTES = 1 << 30
 
 
 def kernel_source_digest():
@@ -51,74 +71,159 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, seconds):
-    """The float64 oracle on whole heads of the workload until ~`seconds` elapse."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
 
-    from oracle import attention_forward
-    from tiled_attention_17_amd.perfmodel import attn_fwd_flops
-    from tiled_attention_17_amd.workloads import to_f64
+def time_launches(fn, stream, n, warm, settle_ms):
+    """Launch fn until settle_ms of GPU time pass, then warm more, then time n launches.
 
-    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    # whole heads, cycling over the workload's heads until the budget is spent
-    done, t0 = 0, time.perf_counter()
-    while True:
-        b, h = heads[done % len(heads)]
-        attention_forward(q[b, h], k[b, h], v[b, h], w.scale)
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
-    threads = max([p.get("num_threads", 1) for p in blas] or [1])
-    flops = attn_fwd_flops(1, done, w.N, w.d)
-    return {
-        "value": flops / el / 1e12,
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{done} head evaluations (the workload has {len(heads)} heads) of {w.name} "
-                  f"(float64 NumPy, S and P materialised), "
-                  f"{el:.1f} s; BLAS threads {threads}, host CPUs {len(os.sched_getaffinity(0))}",
-        "seconds": el,
-    }
-
-
-def _time_ms(fn, stream, warm, n):
-    """Average milliseconds of fn() over n calls after warm calls (HIP events on `stream`)."""
-    import torch
-    for _ in range(warm):
-        fn()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(n):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n
-
-
-def measure_ex(ta, pm, dev, stream, n):
-    """Figures of the masked and unequal-length paths (not the headline metric).
-
-    causal: forward and backward at the headline shape, TFLOP/s over the
-    visible (query, key) pairs (4 d resp. 10 d FLOPs per pair); shard: one
-    device's 2048 queries of a 16384-long sequence against all its keys
-    (library-chosen key splits); decode: one query per sequence against 8192
-    keys, bound by reading K and V (GB/s against 8 TB/s); mxfp8: the MXFP8
-    forward at the headline shape against the fp8 dense peak.
+    Each timed launch has its own start and end event on `stream`; returns
+    per-launch mean / median / min, the whole region's time per launch, and
+    what the settle did.
     """
     import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    torch.cuda.synchronize()
+    spent, settle_launches, batch = 0.0, 0, 2
+    while spent < settle_ms:
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(batch):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b)
+        spent += ms
+        settle_launches += batch
+        if ms < 20.0:  # keep the queue full without syncing after every few launches
+            batch = min(2 * batch, 4096)
+    for _ in range(warm):
+        fn()
+    starts, ends = [ev() for _ in range(n)], [ev() for _ in range(n)]
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(n):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return {"kernel_ms_mean": sum(per) / n, "kernel_ms_median": per[n // 2], "kernel_ms_min": per[0],
+            "ms_per_launch": t0.elapsed_time(t1) / n, "launches": n, "warmup": warm,
+            "settle_ms": spent, "settle_launches": settle_launches}
 
-    from tiled_attention_17_amd.workloads import EXTRA_WORKLOADS, make_inputs
 
+def time_cold(fn, stream, n, scratch):
+    """Per-launch time with the caches evicted before each launch (1 GiB scratch write)."""
+    import torch
+    per = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        per.append(a.elapsed_time(b))
+    per.sort()
+    return {"kernel_ms_median": per[n // 2], "kernel_ms_mean": sum(per) / n, "kernel_ms_min": per[0],
+            "launches": n, "evict_bytes": scratch.numel()}
+
+
+def _rates(pm, flops, nbytes, ms, dt):
+    peak = pm.MI355X_PEAK_FLOPS[dt]
+    return {"tflops": flops / (ms * 1e-3) / 1e12, f"pct_of_{dt}_dense_peak": 100.0 * flops / (ms * 1e-3) / peak,
+            "gb_per_s": nbytes / (ms * 1e-3) / 1e9,
+            "pct_of_hbm": 100.0 * nbytes / (ms * 1e-3) / pm.MI355X_HBM_BYTES_PER_S}
+
+
+# ---------------------------------------------------------------------------
+# measurements (each returns its figures and what the CPU leg should check)
+# ---------------------------------------------------------------------------
+
+def _rows_sample(n, count, seed):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, n // 2, n - 1], rng.integers(0, n, count)]))
+
+
+def measure_backward(ta, pm, dev, stream, n, settle_ms, checks):
+    import torch
+
+    from tiled_attention_17_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[4]
+    x_cpu = make_inputs(w)
+    x = {k: t.to(dev) for k, t in x_cpu.items()}
+    o, lse = ta.attn_fwd(x["q"], x["k"], x["v"], w.scale)
+    g = [torch.empty_like(o) for _ in range(3)]
+    ws = torch.empty(max(ta.attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d), 16), dtype=torch.uint8, device=dev)
+
+    def bwd():
+        ta.attn_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, dq=g[0], dk=g[1], dv=g[2], workspace=ws)
+
+    t = time_launches(bwd, stream, n, 3, settle_ms)
+    ms = t["kernel_ms_mean"]
+    fl = pm.attn_bwd_flops(w.B, w.H, w.N, w.d)
+    r = {"workload": w.name, **t, **_rates(pm, fl, pm.attn_bwd_bytes(w.B, w.H, w.N, w.d, 2), ms, "bf16"),
+         "flops_counted": "10·B·H·N²·d"}
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    checks.append({"name": w.name, "kind": "bwd", "x": x_cpu, "scale": w.scale, "heads": heads,
+                   "o": o.cpu(), "lse": lse.cpu(), "grads": [t.cpu() for t in g]})
+    return r
+
+
+def measure_configs(ta, pm, dev, stream, n, settle_ms, checks):
+    """fp32 single head (cfg 1), d = 64 multi-head (cfg 2), long sequence with spread scores (cfg 4)."""
+    import torch
+
+    from tiled_attention_17_amd.workloads import WORKLOADS, make_inputs
     out = {}
-    peak = pm.MI355X_PEAK_FLOPS["bf16"] / 1e12
+    scratch = torch.empty(COLD_SCRATCH_BYTES, dtype=torch.uint8, device=dev)
+    for w, key in ((WORKLOADS[0], "fp32_small"), (WORKLOADS[1], "d64"), (WORKLOADS[3], "long")):
+        x_cpu = make_inputs(w)
+        x = {k: t.to(dev) for k, t in x_cpu.items()}
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def fwd():
+            ta.attn_fwd(x["q"], x["k"], x["v"], w.scale, out=o, lse=lse)
+
+        long = w.N > 4096
+        t = time_launches(fwd, stream, max(5, n // 10) if long else n, 3, settle_ms)
+        dt = "fp32" if w.dtype == "fp32" else "bf16"
+        eb = 4 if dt == "fp32" else 2
+        fl = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
+        nb = pm.attn_fwd_bytes(w.B, w.H, w.N, w.d, eb)
+        r = {"workload": w.name, "cache": "warm (inputs resident in L2 / Infinity Cache across launches)",
+             **t, **_rates(pm, fl, nb, t["kernel_ms_mean"], dt), "algorithmic_bytes": nb}
+        if not long:
+            c = time_cold(fwd, stream, n, scratch)
+            r["cold"] = {**c, **_rates(pm, fl, nb, c["kernel_ms_median"], dt)}
+        out[key] = r
+        chk = {"name": w.name, "kind": "fwd", "x": x_cpu, "scale": w.scale}
+        if long:  # sampled rows of every head; whole-output parity is in the tests
+            rows = _rows_sample(w.N, 60, 4)
+            chk.update(rows=rows, o=o[:, :, rows].cpu(), lse=lse[:, :, rows].cpu())
+        else:
+            chk.update(o=o.cpu(), lse=lse.cpu())
+        checks.append(chk)
+        del x, o, lse
+    del scratch
+    return out
+
+
+def measure_ex(ta, pm, dev, stream, n, settle_ms, checks):
+    """Causal, query shard, decode (masked and unequal-length paths) and the MXFP8 forward."""
+    import torch
+
+    from tiled_attention_17_amd.workloads import EXTRA_WORKLOADS, HEADLINE, make_inputs
+    out = {}
     for w in EXTRA_WORKLOADS:
-        x = {k: t.to(dev) for k, t in make_inputs(w, with_grad_output=w.causal).items()}
+        x_cpu = make_inputs(w, with_grad_output=w.causal)
+        x = {k: t.to(dev) for k, t in x_cpu.items()}
         o = torch.empty_like(x["q"])
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
         splits = 1 if w.causal else ta.attn_fwd_ex_auto_splits(w.B, w.H, w.Nq, w.Nk, w.d)
@@ -129,32 +234,33 @@ def measure_ex(ta, pm, dev, stream, n):
             ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=w.causal, num_splits=splits,
                            out=o, lse=lse, workspace=ws)
 
-        ms = _time_ms(fwd, stream, 3 * n, n)
+        t = time_launches(fwd, stream, n, 3, settle_ms)
         fl = pm.attn_fwd_flops_masked(w.B, w.H, w.Nq, w.Nk, w.d, w.causal)
-        nbytes = pm.attn_fwd_bytes_ex(w.B, w.H, w.Nq, w.Nk, w.d, 2)
-        r = {"workload": w.name, "splits": splits, "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
-             "pct_of_bf16_dense_peak": 100.0 * fl / (ms * 1e-3) / 1e12 / peak,
-             "gb_per_s": nbytes / (ms * 1e-3) / 1e9,
-             "pct_of_hbm": 100.0 * nbytes / (ms * 1e-3) / pm.MI355X_HBM_BYTES_PER_S}
+        nb = pm.attn_fwd_bytes_ex(w.B, w.H, w.Nq, w.Nk, w.d, 2)
+        r = {"workload": w.name, "splits": splits, **t, **_rates(pm, fl, nb, t["kernel_ms_mean"], "bf16")}
         if w.causal:
             g = [torch.empty_like(x["q"]) for _ in range(3)]
-            bws = torch.empty(ta.attn_bwd_workspace_bytes(w.B, w.H, w.Nq, w.d), dtype=torch.uint8,
+            bws = torch.empty(max(ta.attn_bwd_workspace_bytes(w.B, w.H, w.Nq, w.d), 16), dtype=torch.uint8,
                               device=dev)
 
             def bwd():
                 ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=True,
                                dq=g[0], dk=g[1], dv=g[2], workspace=bws)
 
-            bms = _time_ms(bwd, stream, 3, max(3, n // 5))
+            tb = time_launches(bwd, stream, n, 3, settle_ms)
             bfl = pm.attn_bwd_flops_masked(w.B, w.H, w.Nq, w.Nk, w.d, True)
-            r.update({"bwd_ms": bms, "bwd_tflops": bfl / (bms * 1e-3) / 1e12})
+            r["bwd"] = {**tb, "tflops": bfl / (tb["kernel_ms_mean"] * 1e-3) / 1e12,
+                        "pct_of_bf16_dense_peak": 100.0 * bfl / (tb["kernel_ms_mean"] * 1e-3)
+                        / pm.MI355X_PEAK_FLOPS["bf16"]}
             del g, bws
         out[w.name.split("_")[0]] = r
+        heads = [(0, 0), (w.B - 1, w.H - 1)]
+        checks.append({"name": w.name, "kind": "fwd", "x": x_cpu, "scale": w.scale, "causal": w.causal,
+                       "heads": heads, "o": o.cpu(), "lse": lse.cpu()})
         del x, o, lse, ws
 
     # MXFP8 forward at the headline shape: inputs quantized beforehand and
     # resident as MXFP8 (the quantizer's own time reported separately)
-    from tiled_attention_17_amd.workloads import HEADLINE
     w = HEADLINE
     x = {k: t.to(dev) for k, t in make_inputs(w).items()}
     q8, qs = ta.attn_quantize_mxfp8(x["q"])
@@ -162,57 +268,137 @@ def measure_ex(ta, pm, dev, stream, n):
     vt8, vts = ta.attn_quantize_mxfp8(x["v"], transpose=True)
     o = torch.empty_like(x["q"])
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    ms = _time_ms(lambda: ta.attn_fwd_mxfp8(q8, qs, k8, ks, vt8, vts, w.scale, out=o, lse=lse), stream,
-                  3 * n, n)
-    qms = _time_ms(lambda: (ta.attn_quantize_mxfp8(x["q"]), ta.attn_quantize_mxfp8(x["k"]),
-                            ta.attn_quantize_mxfp8(x["v"], transpose=True)), stream, 3, n)
+    t = time_launches(lambda: ta.attn_fwd_mxfp8(q8, qs, k8, ks, vt8, vts, w.scale, out=o, lse=lse), stream,
+                      n, 3, settle_ms)
+    tq = time_launches(lambda: (ta.attn_quantize_mxfp8(x["q"]), ta.attn_quantize_mxfp8(x["k"]),
+                                ta.attn_quantize_mxfp8(x["v"], transpose=True)), stream, n, 3, 0.0)
     fl = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
-    out["mxfp8"] = {"workload": w.name + " (MXFP8 Q, K, V^T)", "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
-                    "pct_of_fp8_dense_peak": 100.0 * fl / (ms * 1e-3) / pm.MI355X_PEAK_FLOPS["fp8"],
-                    "quantize_q_k_vt_ms": qms}
+    out["mxfp8"] = {"workload": w.name + " (MXFP8 Q, K, V^T)", **t,
+                    "tflops": fl / (t["kernel_ms_mean"] * 1e-3) / 1e12,
+                    "pct_of_fp8_dense_peak": 100.0 * fl / (t["kernel_ms_mean"] * 1e-3) / pm.MI355X_PEAK_FLOPS["fp8"],
+                    "quantize_q_k_vt_ms": tq["ms_per_launch"]}
     return out
 
 
-def measure_configs(ta, pm, dev, stream, n):
-    """The other forward configurations (not the headline metric).
+# ---------------------------------------------------------------------------
+# CPU leg: the oracle as a timed baseline, and the check of the measured outputs
+# ---------------------------------------------------------------------------
 
-    fp32 single head (B=1 H=1 N=256 d=64, against the fp32 MFMA peak), the
-    d = 64 multi-head case (B=4 H=8 N=1024) and the long sequence with
-    spread scores (B=1 H=16 N=16384 d=128, Q ~ N(0, 3^2)), each with
-    library-chosen tiles and one launch per step.
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _max_abs(a, b):
+    import numpy as np
+    return float(np.max(np.abs(a - b))) if b.size else 0.0
+
+
+def _lse_err(got, want):
+    import numpy as np
+    empty = np.isneginf(want)
+    if not np.array_equal(np.isneginf(got), empty):
+        return float("inf")
+    return _max_abs(got[~empty], want[~empty]) if (~empty).any() else 0.0
+
+
+def cpu_leg(w, x_cpu, o_gpu, lse_gpu, seconds, checks):
+    """(cpu_baseline, verification) -- the only part of bench.py that runs the oracle.
+
+    Baseline: the float64 oracle on whole heads of the headline workload,
+    cycling over its heads until ~`seconds` of oracle time are spent; each
+    head it computes is also compared with the GPU's output of the timed
+    launches. Verification: every record in `checks` against the oracle.
+    Bars: bf16 O, dQ, dK, dV max abs error <= 2e-2, fp32 O <= 1e-5, LSE <= 1e-3.
     """
-    import torch
+    import numpy as np
+    from threadpoolctl import threadpool_info
 
-    from tiled_attention_17_amd.workloads import WORKLOADS, make_inputs
+    from oracle import attention_backward, attention_forward
+    from tiled_attention_17_amd.perfmodel import attn_fwd_flops
+    from tiled_attention_17_amd.workloads import to_f64
 
-    out = {}
-    for w, key in ((WORKLOADS[0], "fp32_small"), (WORKLOADS[1], "d64"), (WORKLOADS[3], "long")):
-        x = {k: t.to(dev) for k, t in make_inputs(w).items()}
-        o = torch.empty_like(x["q"])
-        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        reps = n if w.N <= 4096 else max(5, n // 10)
-        ms = _time_ms(lambda: ta.attn_fwd(x["q"], x["k"], x["v"], w.scale, out=o, lse=lse), stream,
-                      3 * reps, reps)
-        fl = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
-        dt = "fp32" if w.dtype == "fp32" else "bf16"
-        peak = pm.MI355X_PEAK_FLOPS[dt] / 1e12
-        tf = fl / (ms * 1e-3) / 1e12
-        out[key] = {"workload": w.name, "ms": ms, "tflops": tf, f"pct_of_{dt}_dense_peak": 100.0 * tf / peak}
-        del x, o, lse
-    return out
+    q, k, v = (to_f64(x_cpu[n]) for n in ("q", "k", "v"))
+    go, gl = to_f64(o_gpu), to_f64(lse_gpu)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, el, errs = 0, 0.0, {}
+    while el < seconds:
+        b, h = heads[done % len(heads)]
+        t0 = time.perf_counter()
+        ro, rl = attention_forward(q[b, h], k[b, h], v[b, h], w.scale)
+        el += time.perf_counter() - t0
+        done += 1
+        if (b, h) not in errs:
+            errs[(b, h)] = (_max_abs(go[b, h], ro), _max_abs(gl[b, h], rl))
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    vendor = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "unknown"
+    flops = attn_fwd_flops(1, done, w.N, w.d)
+    baseline = {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} head evaluations (the workload has {len(heads)} heads) of {w.name} "
+                  f"(float64 NumPy, S and P materialised), {el:.1f} s of oracle time; BLAS threads {threads}, "
+                  f"host CPUs {len(os.sched_getaffinity(0))}",
+        "seconds": el,
+        "cpu_model": _cpu_model(),
+        "blas": vendor,
+    }
+
+    bars = {"bf16": 2e-2, "fp32": 1e-5, "lse": 1e-3}
+    ver = {w.name: {"heads_checked": len(errs), "rows": "all",
+                    "max_abs_err_O": max(e[0] for e in errs.values()),
+                    "max_abs_err_LSE": max(e[1] for e in errs.values())}}
+    for c in checks:
+        t0 = time.perf_counter()
+        x = {n: to_f64(t) for n, t in c["x"].items()}
+        o, lse = to_f64(c["o"]), to_f64(c["lse"])
+        B, H = x["q"].shape[:2]
+        hs = c.get("heads") or [(b, h) for b in range(B) for h in range(H)]
+        rows = c.get("rows")
+        eo = el_ = 0.0
+        grads = [0.0, 0.0, 0.0]
+        for (b, h) in hs:
+            qi = x["q"][b, h] if rows is None else x["q"][b, h][rows]
+            ro, rl = attention_forward(qi, x["k"][b, h], x["v"][b, h], c["scale"], causal=c.get("causal", False))
+            eo = max(eo, _max_abs(o[b, h], ro))
+            el_ = max(el_, _lse_err(lse[b, h], rl))
+            if c["kind"] == "bwd":
+                ref = attention_backward(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h], c["scale"])
+                for i, (gt, rt) in enumerate(zip(c["grads"], ref)):
+                    grads[i] = max(grads[i], _max_abs(to_f64(gt[b, h]), rt))
+        r = {"heads_checked": len(hs), "rows": "all" if rows is None else f"{len(rows)} sampled per head",
+             "max_abs_err_O": eo, "max_abs_err_LSE": el_, "oracle_s": time.perf_counter() - t0}
+        if c["kind"] == "bwd":
+            r.update({"max_abs_err_dQ": grads[0], "max_abs_err_dK": grads[1], "max_abs_err_dV": grads[2]})
+        ver[c["name"]] = r
+    ok = True
+    for name, r in ver.items():
+        tol = bars["fp32"] if "fp32" in name else bars["bf16"]
+        good = all(r.get(f"max_abs_err_{n}", 0.0) <= tol for n in ("O", "dQ", "dK", "dV")) \
+            and r["max_abs_err_LSE"] <= bars["lse"]
+        r["pass"] = bool(good)
+        ok = ok and good
+    return baseline, {"bars": bars, "pass": ok, "workloads": ver}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # The warm-up is long on purpose: under sustained load the MI355X raises
-    # its shader clock over tens of milliseconds (measured on this kernel:
-    # ~1.85 GHz after 10 launches, a steady ~2.05 GHz after ~100 ms), so a
-    # short warm-up times the clock ramp rather than the kernel.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="GPU time of headline launches before the warm-up (clock settle)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="CPU work budget of the oracle baseline (0 disables it)")
+                    help="oracle time of the CPU baseline (0 disables the CPU leg and the output check)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward figures in 'extra'")
     ap.add_argument("--no-ex", action="store_true",
                     help="skip the causal / unequal-length / decoding / other-configuration figures in 'extra'")
@@ -228,7 +414,7 @@ def main():
 
     import tiled_attention_17_amd as ta
     from tiled_attention_17_amd import perfmodel as pm
-    from tiled_attention_17_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+    from tiled_attention_17_amd.workloads import HEADLINE, make_inputs
 
     w = HEADLINE
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -243,68 +429,35 @@ def main():
     def step():
         ta.attn_fwd(x["q"], x["k"], x["v"], w.scale, out=o, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for i in range(K):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per_launch = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
-    total_ms = ev[0].elapsed_time(ev[K])
-    ms_per_step = total_ms / K
+    t = time_launches(step, stream, K, args.warmup, args.settle_ms)
+    o_timed, lse_timed = o.cpu(), lse.cpu()  # every launch writes the same result
+    ms_per_step = t["ms_per_launch"]
     flops = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    kernel_ms = sum(per_launch) / K
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    achieved = flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
     peak = pm.MI355X_PEAK_FLOPS["bf16"] / 1e12
+    nbytes = pm.attn_fwd_bytes(w.B, w.H, w.N, w.d, 2)
 
     extra = {
         "pct_of_bf16_dense_peak": 100.0 * value / peak,
-        "kernel_ms_min": min(per_launch),
-        "kernel_ms_median": sorted(per_launch)[K // 2],
-        "algorithmic_bytes_per_launch": pm.attn_fwd_bytes(w.B, w.H, w.N, w.d, 2),
+        "settle_ms": t["settle_ms"],
+        "settle_launches": t["settle_launches"],
+        "kernel_ms_mean": t["kernel_ms_mean"],
+        "kernel_ms_median": t["kernel_ms_median"],
+        "kernel_ms_min": t["kernel_ms_min"],
+        "algorithmic_bytes_per_launch": nbytes,
+        "gb_per_s": nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9,
+        "timing": "per-launch start/end HIP events on the launch stream after a clock settle; "
+                  "headline launches before the timed ones: settle_launches + warmup",
     }
+    checks = []
+    sub = max(20, K // 4)
     if not args.no_bwd:
-        wb = WORKLOADS[4]
-        xb = {n: t.to(dev) for n, t in make_inputs(wb).items()}
-        ob, lb = ta.attn_fwd(xb["q"], xb["k"], xb["v"], wb.scale)
-        g = [torch.empty_like(ob) for _ in range(3)]
-        ws = torch.empty(ta.attn_bwd_workspace_bytes(wb.B, wb.H, wb.N, wb.d), dtype=torch.uint8,
-                         device=dev)
-
-        def bstep():
-            ta.attn_bwd(xb["q"], xb["k"], xb["v"], ob, xb["do"], lb, wb.scale, dq=g[0], dk=g[1],
-                        dv=g[2], workspace=ws)
-
-        for _ in range(3):
-            bstep()
-        torch.cuda.synchronize()
-        nb = max(3, K // 5)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(nb):
-            bstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / nb
-        extra.update({
-            "bwd_workload": wb.name,
-            "bwd_ms": bms,
-            "bwd_tflops_10BHN2d": pm.attn_bwd_flops(wb.B, wb.H, wb.N, wb.d) / (bms * 1e-3) / 1e12,
-            "fwd_plus_bwd_tflops_14BHN2d": pm.attn_fwd_flops(wb.B, wb.H, wb.N, wb.d) * 3.5
-            / ((ms_per_step + bms) * 1e-3) / 1e12,
-        })
-        del xb, ob, lb, g, ws
-
+        extra["bwd"] = measure_backward(ta, pm, dev, stream, sub, 150.0, checks)
     if not args.no_ex:
-        extra.update(measure_ex(ta, pm, dev, stream, max(20, K // 4)))
-        extra.update(measure_configs(ta, pm, dev, stream, max(20, K // 4)))
+        extra.update(measure_ex(ta, pm, dev, stream, sub, 150.0, checks))
+        extra.update(measure_configs(ta, pm, dev, stream, sub, 150.0, checks))
 
     traffic = measured_traffic()
     result = {
@@ -328,9 +481,14 @@ def main():
         "cpu_baseline": None,
         "extra": extra,
     }
+    ok = True
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, x_cpu, args.cpu_seconds)
+        result["cpu_baseline"], extra["verify"] = cpu_leg(w, x_cpu, o_timed, lse_timed, args.cpu_seconds, checks)
+        ok = extra["verify"]["pass"]
     print(json.dumps(result), flush=True)
+    if not ok:
+        print("bench.py: a measured output is outside the oracle bars (see extra.verify)", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

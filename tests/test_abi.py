@@ -226,3 +226,33 @@ def test_mxfp8_rejects():
     p3[1] = p3[1] + 2  # q_scales not 4-byte aligned
     assert fw(*p3, 1, 2, 128, 128, 0.1, None) == 1 and "aligned" in _err()
     assert fw(*p, 0, 2, 128, 128, 0.1, None) == 0
+
+
+def test_binding_checks_caller_outputs():
+    # Caller-supplied outputs are checked before any call (the C ABI cannot see
+    # tensor sizes): a wrong shape, dtype or layout raises, whatever the device.
+    torch = pytest.importorskip("torch")
+    B, H, N, d = 1, 2, 64, 64
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)  # noqa: E731
+    args = (u8(B, H, N, d), u8(B, H, N, d // 32), u8(B, H, N, d), u8(B, H, N, d // 32),
+            u8(B, H, d, N), u8(B, H, d, N // 32))
+    with pytest.raises(ValueError, match="out"):
+        ta.attn_fwd_mxfp8(*args, out=torch.zeros(B, H, N, d + 1, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="out"):
+        ta.attn_fwd_mxfp8(*args, out=torch.zeros(B, H, N, d, dtype=torch.float32))
+    with pytest.raises(ValueError, match="lse"):
+        ta.attn_fwd_mxfp8(*args, lse=torch.zeros(B, H, N - 1))
+    with pytest.raises(ValueError, match="lse"):
+        ta.attn_fwd_mxfp8(*args, lse=torch.zeros(B, H, N, dtype=torch.float64))
+    with pytest.raises(ValueError, match="lse"):
+        ta.attn_fwd_mxfp8(*args, lse=torch.zeros(B, H, 2 * N)[:, :, ::2])
+    parts = torch.zeros(3, B, H, N, d)
+    lparts = torch.zeros(3, B, H, N)
+    with pytest.raises(ValueError, match="lse"):
+        ta.attn_merge(parts, lparts, lse=torch.zeros(B, H, N + 1))
+    with pytest.raises(ValueError, match="lse"):
+        ta.attn_merge(parts, lparts, lse=torch.zeros(B, H, N, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out"):
+        ta.attn_merge(parts, lparts, out=torch.zeros(B, H, N, d // 2, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        ta.attn_merge(parts, lparts)

@@ -21,6 +21,7 @@ torch = pytest.importorskip("torch")
 
 import tiled_attention_17_amd as ta  # noqa: E402
 from oracle import attention_backward, attention_forward  # noqa: E402
+from oracle_pool import backward_all, forward_all  # noqa: E402
 from tiled_attention_17_amd.workloads import WORKLOADS, Workload, make_inputs, to_f64  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -141,8 +142,15 @@ def test_bwd_bf16_small(B, H, N, d):
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads in the benchmark's launch configuration, sampled
+# full-size workloads in the benchmark's launch configuration, whole outputs
 # ---------------------------------------------------------------------------
+
+def _check_all(name, go, gl, ro, rl, tol, rel):
+    """Every element of O and LSE, reported per head."""
+    for (b, h) in np.ndindex(*ro.shape[:2]):
+        _assert_close(f"{name} O[{b},{h}]", go[b, h], ro[b, h], tol, rel)
+        _assert_close(f"{name} LSE[{b},{h}]", gl[b, h], rl[b, h], LSE_TOL)
+
 
 def test_workload_fp32_single_head_full():
     w = WORKLOADS[0]
@@ -152,39 +160,50 @@ def test_workload_fp32_single_head_full():
     _check_fwd(x, o, lse, w.scale, FP32_TOL, None)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("idx", [1, 2])
-def test_workload_bf16_full_heads_sampled(idx):
+def test_workload_bf16_full_every_head(idx):
+    # B=4 H=8 N=1024 d=64 and the headline B=2 H=16 N=4096 d=128: every
+    # element of O and LSE against the oracle.
     w = WORKLOADS[idx]
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd(x["q"], x["k"], x["v"], w.scale)
     torch.cuda.synchronize()
-    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]
-    _check_fwd(x, o, lse, w.scale, BF16_TOL, BF16_REL, heads=heads)
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    ro, rl = forward_all(q, k, v, w.scale)
+    _check_all(w.name, to_f64(o), to_f64(lse), ro, rl, BF16_TOL, BF16_REL)
 
 
-def test_workload_long_sequence_rows_sampled():
+@pytest.mark.timeout(900)
+def test_workload_long_sequence_every_row():
+    # B=1 H=16 N=16384 d=128, Q ~ N(0, 3^2): all 16 x 16384 rows, the oracle
+    # taken in blocks of 1024 query rows against all keys.
     w = WORKLOADS[3]
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd(x["q"], x["k"], x["v"], w.scale)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N - 1], rng.integers(0, w.N, 120)]))
-    _check_fwd(x, o, lse, w.scale, BF16_TOL, BF16_REL, rows=rows, heads=[(0, 0), (0, 7), (0, 15)])
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    ro, rl = forward_all(q, k, v, w.scale, row_block=1024)
+    _check_all(w.name, to_f64(o), to_f64(lse), ro, rl, BF16_TOL, BF16_REL)
 
 
-def test_workload_fwd_bwd_full_heads_sampled():
+@pytest.mark.timeout(900)
+def test_workload_fwd_bwd_every_head():
+    # B=2 H=16 N=4096 d=128 forward and backward: every element of O, LSE,
+    # dQ, dK and dV against the oracle.
     w = WORKLOADS[4]
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd(x["q"], x["k"], x["v"], w.scale)
     dq, dk, dv = ta.attn_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale)
     torch.cuda.synchronize()
     q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
-    _check_fwd(x, o, lse, w.scale, BF16_TOL, BF16_REL, heads=[(0, 0), (1, 15)])
-    g = [to_f64(t) for t in (dq, dk, dv)]
-    for (b, h) in [(0, 0), (1, 15)]:
-        ref = attention_backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale)
-        for name, got, want in zip(("dQ", "dK", "dV"), g, ref):
-            _assert_close(f"{name}[{b},{h}]", got[b, h], want, BF16_TOL, BF16_REL)
+    ro, rl = forward_all(q, k, v, w.scale)
+    _check_all(w.name, to_f64(o), to_f64(lse), ro, rl, BF16_TOL, BF16_REL)
+    ref = backward_all(q, k, v, do, w.scale)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        got = to_f64(got)
+        for (b, h) in np.ndindex(w.B, w.H):
+            _assert_close(f"{name}[{b},{h}]", got[b, h], want[b, h], BF16_TOL, BF16_REL)
 
 
 # ---------------------------------------------------------------------------

@@ -15,6 +15,7 @@ torch = pytest.importorskip("torch")
 
 import tiled_attention_17_amd as ta  # noqa: E402
 from oracle import attention_forward, merge_partials  # noqa: E402
+from oracle_pool import backward_all, forward_all  # noqa: E402
 from tiled_attention_17_amd.workloads import EXTRA_WORKLOADS, Workload, make_inputs, to_f64  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -327,34 +328,45 @@ def test_merge_of_gpu_key_ranges_equals_whole():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads of these paths, sampled
+# full-size workloads of these paths, whole outputs
 # ---------------------------------------------------------------------------
 
-def test_workload_causal_full_heads_sampled():
+def _check_whole(x, o, lse, scale, causal, row_block=None):
+    """Every element of O and LSE against the oracle (evaluated in a thread pool)."""
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    ro, rl = forward_all(q, k, v, scale, causal=causal, row_block=row_block)
+    go, gl = to_f64(o), to_f64(lse)
+    for (b, h) in np.ndindex(*q.shape[:2]):
+        empty = np.isneginf(rl[b, h])
+        assert np.all(go[b, h][empty] == 0), f"O[{b},{h}]: rows without keys are not 0"
+        _assert_o(f"O[{b},{h}]", go[b, h], ro[b, h], BF16_TOL, BF16_REL)
+        _assert_lse(f"LSE[{b},{h}]", gl[b, h], rl[b, h])
+
+
+@pytest.mark.timeout(600)
+def test_workload_causal_every_head():
     w = EXTRA_WORKLOADS[0]
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
     torch.cuda.synchronize()
-    _check(x, o, lse, w.scale, True, BF16_TOL, BF16_REL, heads=[(0, 0), (1, 15), (1, 6)])
+    _check_whole(x, o, lse, w.scale, True)
 
 
-def test_workload_shard_rows_sampled():
+@pytest.mark.timeout(600)
+def test_workload_shard_every_row():
     w = EXTRA_WORKLOADS[1]
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=0)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, w.Nq - 1], rng.integers(0, w.Nq, 100)]))
-    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL, heads=[(0, 0), (0, 9), (0, 15)], rows=rows)
+    _check_whole(x, o, lse, w.scale, False, row_block=1024)
 
 
-def test_workload_decode_heads_sampled():
+def test_workload_decode_every_head():
     w = EXTRA_WORKLOADS[2]
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=0)
     torch.cuda.synchronize()
-    heads = [(0, 0), (7, 15), (3, 4), (5, 11)]
-    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL, heads=heads)
+    _check_whole(x, o, lse, w.scale, False)
 
 
 # ---------------------------------------------------------------------------
@@ -404,12 +416,18 @@ def test_bwd_ex_empty_sides():
     assert torch.all(dq2 == 0) and dk2.numel() == 0
 
 
-def test_workload_causal_fwd_bwd_heads_sampled():
-    # Causal attention at the forward + backward workload's shape.
+@pytest.mark.timeout(900)
+def test_workload_causal_fwd_bwd_every_head():
+    # Causal attention at the forward + backward workload's shape, every head.
     w = _wl(2, 16, 4096, 4096, 128, seed=5, causal=True)
     x = _cuda(make_inputs(w, with_grad_output=True))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True)
     dq, dk, dv = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=True)
     torch.cuda.synchronize()
-    _check(x, o, lse, w.scale, True, BF16_TOL, BF16_REL, heads=[(0, 0), (1, 15)])
-    _check_bwd(x, dq, dk, dv, w.scale, True, heads=[(0, 0), (1, 15)])
+    _check_whole(x, o, lse, w.scale, True)
+    q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    ref = backward_all(q, k, v, do, w.scale, causal=True)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        got = to_f64(got)
+        for (b, h) in np.ndindex(w.B, w.H):
+            _assert_o(f"{name}[{b},{h}]", got[b, h], want[b, h], BF16_TOL, BF16_REL)

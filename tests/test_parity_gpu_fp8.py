@@ -7,8 +7,9 @@ transposed column blocks (V^T).
 Forward: the inputs are quantized on the CPU by the oracle (so no expected
 value comes from the GPU path), the GPU runs attn_fwd_mxfp8 on those codes,
 and the oracle computes attention on the dequantized inputs. The kernel also
-rounds P to E4M3 (relative error <= 2^-4 per element) before O = P V, and O
-to bf16 (<= 2^-9 relative), so every element must satisfy
+rounds P to E4M3 (unit roundoff 2^-4: 4 significant bits) before O = P V,
+and O to bf16 (unit roundoff 2^-8: 8 significant bits), so every element
+must satisfy
   |O - O_ref| <= 2^-4 (P |V_hat|) + 2^-8 |O_ref| + 2^-12 max|V_hat| + 1e-4,
 (the third term covers probabilities far below their block's maximum, which
 E4M3 holds as subnormals); LSE uses the unrounded probabilities and keeps

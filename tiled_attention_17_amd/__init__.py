@@ -20,7 +20,11 @@ __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_e
            "library", "AttnError",
            "ATTN_BF16", "ATTN_FP32", "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "LIB_PATH"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtiledattn.so")
+# TILED_ATTN_LIBRARY=ordered selects the debug build whose LDS transfers are
+# all ordered by the compiler (see build.py); the default is the release build.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libtiledattn_ordered.so" if os.environ.get("TILED_ATTN_LIBRARY") == "ordered"
+                        else "libtiledattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_BF16, ATTN_FP32 = 0, 1
@@ -142,8 +146,7 @@ def attn_fwd(q, k, v, scale=None, *, out=None, lse=None, stream=None):
     _shape4("out", out, shape, dt, dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _lse_out(lse, (B, H, N), dev)
     with torch.cuda.device(dev):
         st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H, N, d, float(scale), _dtype_code(q), _stream(dev, stream))
@@ -190,8 +193,7 @@ def attn_fwd_ex(q, k, v, scale=None, *, causal=False, num_splits=1, out=None, ls
     _shape4("out", out, (B, H, Nq, d), dt, dev)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
-    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    _lse_out(lse, (B, H, Nq), dev)
     code = _dtype_code(q)
     mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
     with torch.cuda.device(dev):
@@ -218,10 +220,17 @@ def attn_merge(o_parts, lse_parts, *, dtype=None, out=None, lse=None, stream=Non
             or not lse_parts.is_contiguous():
         raise ValueError("lse_parts must be a contiguous float32 [P, B, H, N] tensor")
     dev = o_parts.device
+    if lse_parts.device != dev:
+        raise ValueError(f"lse_parts is on {lse_parts.device}, expected {dev}")
     dtype = torch.bfloat16 if dtype is None else dtype
+    if out is not None:
+        _shape4("out", out, (B, H, N, d), dtype, dev)
+    if lse is not None:
+        _lse_out(lse, (B, H, N), dev)
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
     if out is None:
         out = torch.empty((B, H, N, d), dtype=dtype, device=dev)
-    _shape4("out", out, (B, H, N, d), dtype, dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
@@ -245,8 +254,7 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, *, dq=None, dk=None, dv=None, work
     for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
         _shape4(name, t, shape, dt, dev)
     B, H, N, d = shape
-    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _lse_out(lse, (B, H, N), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -281,8 +289,7 @@ def attn_bwd_ex(q, k, v, o, do, lse, scale=None, *, causal=False, dq=None, dk=No
     _shape4("v", v, (B, H, Nk, d), dt, dev)
     for name, t in (("o", o), ("do", do)):
         _shape4(name, t, (B, H, Nq, d), dt, dev)
-    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    _lse_out(lse, (B, H, Nq), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -360,11 +367,21 @@ def attn_quantize_mxfp8(x, *, transpose=False, stream=None):
     return q, sc
 
 
+def _lse_out(lse, shape, device):
+    """Checks a caller-supplied LSE output: a contiguous float32 tensor of `shape` on `device`."""
+    import torch
+    if tuple(lse.shape) != shape or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != device:
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {shape} on {device}")
+
+
 def attn_fwd_mxfp8(q8, q_scales, k8, k_scales, vt8, vt_scales, scale=None, *, out=None, lse=None,
                    stream=None):
     """O (bf16), LSE of MXFP8 attention (see attn_fwd_mxfp8). q8, k8 [B,H,N,d]; vt8 [B,H,d,N]."""
     import torch
     lib = library()
+    if q8.dim() != 4:
+        raise ValueError(f"q8 must be [B, H, N, d], got {tuple(q8.shape)}")
     B, H, N, d = q8.shape
     shapes = {"q8": (q8, (B, H, N, d)), "q_scales": (q_scales, (B, H, N, d // 32)),
               "k8": (k8, (B, H, N, d)), "k_scales": (k_scales, (B, H, N, d // 32)),
@@ -372,6 +389,10 @@ def attn_fwd_mxfp8(q8, q_scales, k8, k_scales, vt8, vt_scales, scale=None, *, ou
     for name, (t, shp) in shapes.items():
         if tuple(t.shape) != shp or t.dtype != torch.uint8 or not t.is_contiguous() or t.device != q8.device:
             raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {shp} on {q8.device}")
+    if out is not None:
+        _shape4("out", out, (B, H, N, d), torch.bfloat16, q8.device)
+    if lse is not None:
+        _lse_out(lse, (B, H, N), q8.device)
     if q8.device.type != "cuda":
         raise ValueError("tensors must be on a GPU device")
     if scale is None:

@@ -1,4 +1,12 @@
-"""Build the HIP library libtiledattn.so in-tree for gfx950 with hipcc."""
+"""Build the HIP library in-tree for gfx950 with hipcc.
+
+libtiledattn.so is the library. libtiledattn_ordered.so is the same sources
+built with TATTN_ORDERED_LDS_DMA: every LDS transfer the kernels order by
+hand goes through the form the compiler orders, with an extra wait and
+barrier where a staged tile is published. It is a debug build for parity
+runs (the binding loads it when TILED_ATTN_LIBRARY=ordered), never the
+measured one.
+"""
 
 from __future__ import annotations
 
@@ -10,6 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtiledattn.so")
+LIB_ORDERED = os.path.join(PKG, "libtiledattn_ordered.so")
 SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "matmul.hip", "attn_fp8.hip"]
 
 FLAGS = [
@@ -25,10 +34,12 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, ordered_lds_dma: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    out = LIB_ORDERED if ordered_lds_dma else LIB
+    tmp = out + ".tmp"
+    defs = ["-DTATTN_ORDERED_LDS_DMA"] if ordered_lds_dma else []
+    cmd = [hipcc, *FLAGS, *defs, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -39,9 +50,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, ordered_lds_dma="--ordered-lds-dma" in sys.argv))

@@ -514,8 +514,7 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     dq_scores_to_ds<MASKED, D>(sacc, dpacc, c, lse2, drow, j * 64, kmax, h, pw);
     if (more) st.store(kts(cur ^ 1), tid);
     pv_tile<D>(kts(cur), pw, vo, dqacc);  // dQ^T += K^T dS^T
-    wait_vmem();
-    __syncthreads();
+    publish_lds();  // next K, V tiles (transfers) and K^T (stores)
   };
   // Key tiles from n_full on are masked (a 256-query tile's mask edge spans
   // up to five 64-key tiles; they run in a loop of their own).

@@ -359,8 +359,7 @@ void attn_fwd_bf16_kernel(const FwdParams p) {
     softmax_tile<MASKED, T::DB>(sacc, p.c, kr.k_begin + j * T::BN, kmax, h, m_run, l_run, oacc, pw);
     pv_tile<D>(vs(cur), pw, vo, oacc);
     if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 0, tid);
-    wait_vmem();  // K tile written to LDS
-    __syncthreads();
+    publish_lds();  // K tile written to LDS by its transfer, V^T by the stores
   };
   // Tiles from n_full on are masked; there are at most kMaxMaskedTiles.
   const int n_plain = min(kr.n_full, n_kt);
@@ -462,8 +461,7 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
                                 oacc, pw);
     pv_tile<D>(vs(cur), pw, vo, oacc);
     if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 0, gtid);
-    wait_vmem();  // K tile written to LDS
-    __syncthreads();
+    publish_lds();  // K tile written to LDS by its transfer, V^T by the stores
   };
   // Only the range's last tile (index n_full of a ragged end, group 1's
   // last) holds keys past the end. Each group runs n_half barriers.
@@ -471,7 +469,7 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
   int i = 0;
   for (; i < n_plain; ++i) step(std::false_type{}, i);
   if (i < my_n) step(std::true_type{}, i++);
-  for (; i < n_half; ++i) __syncthreads();
+  for (; i < n_half; ++i) publish_lds();  // the same barriers as a working step
 
   // Hand-over: group 1's lane values to LDS ([wave][element][lane]), group 0 merges.
   float* xb = (float*)smem + (size_t)wave * NE * 64 + lane;

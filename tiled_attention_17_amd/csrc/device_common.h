@@ -84,6 +84,17 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, i
                                            0, 0, 0);
 }
 
+// Debug build option TATTN_ORDERED_LDS_DMA: every transfer below goes
+// through the intrinsic the compiler orders, and each point that publishes a
+// staged tile (publish_lds) also waits for every counter and takes a second
+// barrier. A parity run of that build checks that the hand-ordered form of
+// the release build computes the same results.
+#ifdef TATTN_ORDERED_LDS_DMA
+constexpr bool kOrderedLdsDma = true;
+#else
+constexpr bool kOrderedLdsDma = false;
+#endif
+
 // The same transfer issued through inline assembly, which the compiler
 // does not see as a write to LDS. For the intrinsic above it conservatively
 // waits for the transfer before any later LDS read of the workgroup's
@@ -96,6 +107,10 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, i
 // and knows its value afterwards (the s_nop keeps a wait state between that
 // write and the transfer that reads it).
 __device__ __forceinline__ void lds_dma16_async(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
+  if (kOrderedLdsDma) {
+    lds_dma16(r, lds, voff);
+    return;
+  }
   const unsigned m = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
   asm volatile(
       "s_nop 0\n\t"
@@ -113,6 +128,18 @@ __device__ __forceinline__ void lds_dma16_async(__amdgpu_buffer_rsrc_t r, bf16* 
 // for them again, counting the tile staged meanwhile as well.)
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left at their maximum
+}
+
+// Publishes the tiles this wave staged (with either transfer form above) to
+// the whole workgroup: its vector-memory operations are waited for, then a
+// workgroup barrier. Every wave of the workgroup must call it.
+__device__ __forceinline__ void publish_lds() {
+  wait_vmem();
+  __syncthreads();
+  if (kOrderedLdsDma) {
+    __builtin_amdgcn_s_waitcnt(0);  // every counter
+    __syncthreads();
+  }
 }
 
 // 8 bf16 from two transposed 4-element LDS reads (see the header comment).

@@ -23,6 +23,15 @@
       instruction, and HBM bytes (FETCH_SIZE + WRITE_SIZE, calibrated on the
       copy) with the achieved GB/s. Writes profiles/kernel_counters.md.
 
+  python -m tiled_attention_17_amd.profiling summarize-bench --trace DIR --bench-line FILE --command CMD
+      Reads the kernel trace (and --stats table) of a rocprofv3 run of
+      bench.py together with the JSON line that run printed, and writes
+      profiles/fwd_bf16_n4096_d128_kernel_stats.md: every kernel's calls and
+      average duration, and the headline forward's timed launches picked out
+      of the trace by launch order (bench.py launches the headline first:
+      settle_launches + warmup untimed launches, then `steps` timed ones),
+      with their average duration and roofline fraction beside the line's.
+
   python -m tiled_attention_17_amd.profiling summarize --fetch DIR --write DIR [--stats DIR]
       Reads the counter CSVs of the two runs (FETCH_SIZE, WRITE_SIZE; KiB per
       dispatch), scales the forward kernel's figures by what the same counter
@@ -319,6 +328,74 @@ def summarize(fetch_dir, write_dir, stats_dir, copy_mib, out_json, out_txt):
     print(json.dumps(res, indent=2))
 
 
+def _csv_rows(d, suffix):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_bench(trace_dir, bench_line, cmd, out_md):
+    """Kernel-trace summary of one bench.py run, with the headline's timed launches picked out."""
+    with open(bench_line) as f:
+        line = next(json.loads(s) for s in f if s.startswith("{"))
+    ex = line["extra"]
+    steps, warm = line["steps"], line["warmup"]
+    untimed = ex["settle_launches"] + warm
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    disp = sorted(((int(r["Dispatch_Id"]), _short(r["Kernel_Name"]),
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in trace))
+    fwd = [ns for _, k, ns in disp if k.startswith(FWD_KERNEL)]
+    timed = fwd[untimed:untimed + steps]
+    if len(timed) != steps:
+        raise SystemExit(f"trace holds {len(fwd)} forward launches, fewer than {untimed} + {steps}")
+    flops = 4 * line["config"]["B"] * line["config"]["H"] * line["config"]["N"] ** 2 * line["config"]["d"]
+    peak = line["roofline"]["peak"] * 1e12
+    avg_us = sum(timed) / steps / 1e3
+    srt = sorted(timed)
+    frac_trace = flops / (avg_us * 1e-6) / peak
+    groups = {}
+    for _, k, ns in disp:
+        g = groups.setdefault(k, [0, 0, None, 0])
+        g[0] += 1
+        g[1] += ns
+        g[2] = ns if g[2] is None else min(g[2], ns)
+        g[3] = max(g[3], ns)
+    lines = [
+        f"# Kernel trace of the benchmark command: headline forward {line['config']['workload']}", "",
+        "Command (repo root on the MI355X box):", "",
+        f"    {cmd}", "",
+        "## Headline forward: the timed launches", "",
+        f"bench.py launched the headline forward {ex['settle_launches']} times to settle the clock "
+        f"({ex['settle_ms']:.0f} ms of GPU time), {warm} warm-up times, then {steps} timed times. "
+        f"The timed launches are forward launches {untimed + 1}..{untimed + steps} of the trace "
+        "(the headline is the first workload bench.py runs).", "",
+        "| figure | kernel trace (timed launches) | bench.py line (HIP events) |",
+        "|---|---|---|",
+        f"| average duration | {avg_us:.1f} us | {ex['kernel_ms_mean'] * 1e3:.1f} us |",
+        f"| median duration | {srt[steps // 2] / 1e3:.1f} us | {ex['kernel_ms_median'] * 1e3:.1f} us |",
+        f"| min duration | {srt[0] / 1e3:.1f} us | {ex['kernel_ms_min'] * 1e3:.1f} us |",
+        f"| TFLOP/s at 4·B·H·N²·d = {flops / 1e9:.1f} GFLOP | {flops / (avg_us * 1e-6) / 1e12:.1f} | "
+        f"{line['roofline']['achieved']:.1f} |",
+        f"| roofline frac (peak {line['roofline']['peak']:.0f} TFLOP/s) | {frac_trace:.4f} | "
+        f"{line['roofline']['frac']:.4f} |", "",
+        f"Line vs trace: {100.0 * (line['roofline']['frac'] / frac_trace - 1):+.1f} % (the events also hold "
+        "the dispatch gap between back-to-back launches).", "",
+        "## Every kernel of the run (rocprofv3 kernel trace; durations in us)", "",
+        "| kernel | calls | average | min | max |", "|---|---|---|---|---|"]
+    for k, (n, tot, mn, mx) in sorted(groups.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| {k} | {n} | {tot / n / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} |")
+    lines += ["", "The forward kernel's average over all its calls also holds the settle launches, the "
+              "warm-up, and the causal, query-shard and long-sequence launches (other shapes), so only "
+              "the timed window above compares with the line.", "",
+              "Bench line of the same run:", "", "    " + json.dumps({k: line[k] for k in (
+                  "value", "ms_per_step", "steps", "warmup", "roofline")})]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:20]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -334,6 +411,11 @@ def main():
     ss.add_argument("--write", required=True)
     ss.add_argument("--copy-mib", type=int, default=1024)
     ss.add_argument("--out-md", default=os.path.join(ROOT, "profiles", "kernel_counters.md"))
+    sb = sub.add_parser("summarize-bench")
+    sb.add_argument("--trace", required=True)
+    sb.add_argument("--bench-line", required=True)
+    sb.add_argument("--command", required=True)
+    sb.add_argument("--out-md", default=os.path.join(ROOT, "profiles", "fwd_bf16_n4096_d128_kernel_stats.md"))
     s = sub.add_parser("summarize")
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
@@ -346,6 +428,8 @@ def main():
         run(a.launches, a.copy_mib)
     elif a.cmd == "run-set":
         run_set(a.launches, a.copy_mib)
+    elif a.cmd == "summarize-bench":
+        summarize_bench(a.trace, a.bench_line, a.command, a.out_md)
     elif a.cmd == "summarize-set":
         summarize_set(a.sq, a.fetch, a.write, a.copy_mib, a.out_md)
     else:
