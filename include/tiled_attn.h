@@ -279,6 +279,27 @@ attn_status attn_bwd_ex(const void* q, const void* k, const void* v, const void*
                         int64_t Nk, int64_t d, float scale, attn_mask mask, attn_dtype dtype,
                         void* stream);
 
+/* Largest B * H * Nq that attn_bwd_ex_noalloc accepts (its fixed scratch). */
+#define ATTN_NOALLOC_MAX_ROWS (1 << 22)
+
+/*
+ * attn_bwd_ex without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Arguments, results and errors are those of attn_bwd_ex
+ * minus the workspace; the caller still provides every input and output.
+ * The per-row terms D_i go to a fixed array of ATTN_NOALLOC_MAX_ROWS floats
+ * (16 MiB) that the library holds on each device it runs on until the
+ * process ends; B * H * Nq above ATTN_NOALLOC_MAX_ROWS returns
+ * ATTN_ERR_UNSUPPORTED. Nothing is allocated, freed or cleared: every D_i a
+ * call reads is written earlier in the same call. All calls on one device
+ * share that array, so calls that overlap in time on one device (different
+ * streams, or host threads) race; serialise them.
+ */
+attn_status attn_bwd_ex_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                attn_mask mask, attn_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

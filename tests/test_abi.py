@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"attn_version", "attn_status_string", "attn_last_error", "attn_fwd",
                           "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
                           "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_ex",
-                          "attn_matmul_nt", "attn_quantize_mxfp8", "attn_fwd_mxfp8"}
+                          "attn_matmul_nt", "attn_quantize_mxfp8", "attn_fwd_mxfp8", "attn_bwd_ex_noalloc"}
     lib = ctypes.CDLL(ta.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -256,3 +256,20 @@ def test_binding_checks_caller_outputs():
         ta.attn_merge(parts, lparts, out=torch.zeros(B, H, N, d // 2, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="GPU"):
         ta.attn_merge(parts, lparts)
+
+
+def test_bwd_noalloc_rejects_before_any_gpu_call():
+    # The size limit and the argument checks of attn_bwd_ex apply before the
+    # library looks up its scratch array (no GPU call happens here).
+    lib = ta.library()
+    p = [A + i * T for i in range(9)]
+    rows = ta.ATTN_NOALLOC_MAX_ROWS
+    assert lib.attn_bwd_ex_noalloc(*p, 1, 1, rows + 1, 64, 64, 0.125, 0, 0, None) == 2
+    assert "allocation-free" in _err() and str(rows) in _err()
+    assert lib.attn_bwd_ex_noalloc(*p, 2, 2, rows // 4 + 64, 64, 64, 0.125, 0, 0, None) == 2
+    assert lib.attn_bwd_ex_noalloc(*p, 1, 2, 128, 256, 64, 0.125, 5, 0, None) == 1 and "unknown mask" in _err()
+    assert lib.attn_bwd_ex_noalloc(*p, 1, 2, 128, 256, 64, 0.125, 0, 1, None) == 2 and "bf16 only" in _err()
+    p2 = list(p)
+    p2[6] = p2[0] + 64  # dq inside q
+    assert lib.attn_bwd_ex_noalloc(*p2, 1, 2, 128, 256, 64, 0.125, 0, 0, None) == 1 and "overlaps" in _err()
+    assert lib.attn_bwd_ex_noalloc(*([0] * 9), 1, 2, 0, 0, 64, 0.125, 0, 0, None) == 0

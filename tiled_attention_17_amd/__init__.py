@@ -16,7 +16,7 @@ import os
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
            "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_matmul_nt",
-           "attn_quantize_mxfp8", "attn_fwd_mxfp8",
+           "attn_quantize_mxfp8", "attn_fwd_mxfp8", "attn_bwd_ex_noalloc", "ATTN_NOALLOC_MAX_ROWS",
            "library", "AttnError",
            "ATTN_BF16", "ATTN_FP32", "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "LIB_PATH"]
 
@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_BF16, ATTN_FP32 = 0, 1
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
+ATTN_NOALLOC_MAX_ROWS = 1 << 22
 
 _lib = None
 
@@ -81,6 +82,10 @@ def library():
                                    c_i64, c_f, c_vp]
     lib.attn_matmul_nt.restype = ctypes.c_int
     lib.attn_matmul_nt.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_vp]
+    lib.attn_bwd_ex_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_ex_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_i64, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int,
+                                        ctypes.c_int, c_vp]
     lib.attn_bwd_ex.restype = ctypes.c_int
     lib.attn_bwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                 ctypes.c_size_t, c_i64, c_i64, c_i64, c_i64, c_i64, c_f, ctypes.c_int,
@@ -308,6 +313,39 @@ def attn_bwd_ex(q, k, v, o, do, lse, scale=None, *, causal=False, dq=None, dk=No
                              _ptr(dk), _ptr(dv), workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d,
                              float(scale), mask, code, _stream(dev, stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def attn_bwd_ex_noalloc(q, k, v, o, do, lse, scale=None, *, causal=False, dq, dk, dv, stream=None):
+    """attn_bwd_ex without a workspace (see attn_bwd_ex_noalloc in tiled_attn.h).
+
+    The caller passes the outputs dq, dk, dv; the library allocates nothing.
+    B * H * Nq must not exceed ATTN_NOALLOC_MAX_ROWS.
+    """
+    lib = library()
+    _shape4("q", q)
+    dt, dev = q.dtype, q.device
+    B, H, Nq, d = q.shape
+    _shape4("k", k, None, dt, dev)
+    Nk = k.shape[2]
+    _shape4("k", k, (B, H, Nk, d), dt, dev)
+    _shape4("v", v, (B, H, Nk, d), dt, dev)
+    for name, t in (("o", o), ("do", do), ("dq", dq)):
+        _shape4(name, t, (B, H, Nq, d), dt, dev)
+    _shape4("dk", dk, (B, H, Nk, d), dt, dev)
+    _shape4("dv", dv, (B, H, Nk, d), dt, dev)
+    _lse_out(lse, (B, H, Nq), dev)
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
+    import torch
+    with torch.cuda.device(dev):
+        st = lib.attn_bwd_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, float(scale), mask,
+                                     _dtype_code(q), _stream(dev, stream))
     _check(st)
     return dq, dk, dv
 

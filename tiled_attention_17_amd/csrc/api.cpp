@@ -394,10 +394,13 @@ attn_status attn_merge(const float* o_parts, const float* lse_parts, int64_t num
 
 namespace {
 
+// noalloc: the allocation-free variant (no workspace argument; the row terms
+// go to the library's fixed per-device array, which bounds B * H * Nq).
 attn_status bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, void* workspace,
                        size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
-                       int64_t d, float scale, int mask, attn_dtype dtype, void* stream) {
+                       int64_t d, float scale, int mask, attn_dtype dtype, void* stream,
+                       bool noalloc = false) {
   int64_t q_elems = 0, q_rows = 0, k_elems = 0, k_rows = 0;
   attn_status s = check_shape(B, H, Nq, d, dtype, &q_elems, &q_rows);
   if (s != ATTN_OK) return s;
@@ -407,18 +410,23 @@ attn_status bwd_common(const void* q, const void* k, const void* v, const void* 
   if ((s = check_scale(scale)) != ATTN_OK) return s;
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown mask %d", mask);
+  if (noalloc && q_rows > tattn::kNoAllocRows)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "B*H*Nq = %lld query rows exceed the allocation-free backward's scratch (%lld rows)",
+                (long long)q_rows, (long long)tattn::kNoAllocRows);
   if (q_rows == 0 && k_rows == 0) return ok();
   // Tensors of zero rows may be NULL; the others must be valid.
+  const int64_t ws_rows = noalloc ? 0 : q_rows;
   const struct { const void* p; const char* n; int64_t rows; } ins[] = {
       {q, "q", q_rows}, {k, "k", k_rows}, {v, "v", k_rows}, {o, "o", q_rows},
       {dout, "dout", q_rows}, {lse, "lse", q_rows}};
   const struct { const void* p; const char* n; int64_t rows; } outs[] = {
-      {dq, "dq", q_rows}, {dk, "dk", k_rows}, {dv, "dv", k_rows}, {workspace, "workspace", q_rows}};
+      {dq, "dq", q_rows}, {dk, "dk", k_rows}, {dv, "dv", k_rows}, {workspace, "workspace", ws_rows}};
   for (auto& x : ins)
     if (x.rows > 0 && (s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
   for (auto& x : outs)
     if (x.rows > 0 && (s = check_ptr(x.p, x.n, 16)) != ATTN_OK) return s;
-  const size_t need = (size_t)q_rows * sizeof(float);
+  const size_t need = (size_t)ws_rows * sizeof(float);
   if (workspace_bytes < need)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
                 workspace_bytes, need);
@@ -443,7 +451,7 @@ attn_status bwd_common(const void* q, const void* k, const void* v, const void* 
   if ((s = device_cus(&cus)) != ATTN_OK) return s;
   tattn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B * H, Nq, Nk, d, scale,
                    mask == ATTN_MASK_CAUSAL, stream, cus};
-  const hipError_t e = tattn::launch_attn_bwd(a);
+  const hipError_t e = noalloc ? tattn::launch_attn_bwd_noalloc(a) : tattn::launch_attn_bwd(a);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -473,6 +481,14 @@ attn_status attn_bwd_ex(const void* q, const void* k, const void* v, const void*
                         void* stream) {
   return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, d,
                     scale, (int)mask, dtype, stream);
+}
+
+attn_status attn_bwd_ex_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                attn_mask mask, attn_dtype dtype, void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, nullptr, 0, B, H, Nq, Nk, d, scale, (int)mask,
+                    dtype, stream, true);
 }
 
 }  // extern "C"

@@ -32,6 +32,8 @@
 // dQ.
 #include <type_traits>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 #include "tile_common.h"
@@ -584,6 +586,48 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
 
 hipError_t launch_attn_bwd(const BwdArgs& a) {
   return a.d == 64 ? launch_bwd_d<64>(a) : launch_bwd_d<128>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the row terms D_i (the only scratch the backward
+// uses) go to this fixed device array. Each device holds its own copy, at
+// its own address; in host code the name is only a stand-in for the symbol,
+// so kernels get the device address hipGetSymbolAddress reports, looked up
+// once per device (with that device current) and kept. The row-dot kernel
+// writes every D_i a call reads before the sweeps read it, so nothing needs
+// clearing between calls; calls that overlap on one device share the array
+// and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kNoAllocRows];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_addr[kMaxScratchDevices];
+
+hipError_t scratch_address(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = (float*)p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_attn_bwd_noalloc(const BwdArgs& a) {
+  if (a.BH * a.Nq > kNoAllocRows) return hipErrorInvalidValue;
+  BwdArgs b = a;
+  const hipError_t e = scratch_address(&b.row_dot);
+  if (e != hipSuccess) return e;
+  return launch_attn_bwd(b);
 }
 
 }  // namespace tattn

@@ -114,6 +114,15 @@ hipError_t launch_mx_quantize(const void* x, int64_t batch, int64_t rows, int64_
 hipError_t launch_matmul_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
                             void* stream);
 hipError_t launch_attn_bwd(const BwdArgs& a);
+
+// Query rows (B * H * N_q) the allocation-free backward accepts: its row
+// terms D_i live in a fixed device array of this many floats (16 MiB), one
+// copy per device for the life of the process.
+constexpr int64_t kNoAllocRows = int64_t(1) << 22;
+// The backward of launch_attn_bwd with a.row_dot ignored: the row terms go
+// to that fixed array instead (a.BH * a.Nq <= kNoAllocRows, checked by the
+// caller). Allocates nothing.
+hipError_t launch_attn_bwd_noalloc(const BwdArgs& a);
 int fwd_bf16_waves(int64_t BH, int64_t Nq, int64_t splits, int num_cus);
 
 }  // namespace tattn
