@@ -100,6 +100,34 @@ def test_fwd_bf16_tile_configs(waves, d, monkeypatch):
     _check_fwd(x, o, lse, w.scale, BF16_TOL, BF16_REL)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_running_max_jumps(d, causal, monkeypatch):
+    # Key rows grow in steps along the sequence, so each row's scores jump far
+    # above the running max mid-sweep: by ~20 (base 2) at key 448 (mid-tile,
+    # in a 32-key block after others of the same tile), by ~70 at key 640 and
+    # by more than fp32's exponent range at key 800 (2^x overflows before the
+    # max is moved). The 256-query ping-pong kernel is forced, whose unmasked
+    # tiles skip the row max until a block's sum shows such a jump.
+    monkeypatch.setenv("TILED_ATTN_FWD_WAVES", "8")
+    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", "1")
+    w = _wl(1, 2, 1000, d, seed=77)
+    x = make_inputs(w)
+    mult = torch.ones(w.N)
+    mult[448:] = 6.0
+    mult[640:] = 20.0
+    mult[800:] = 60.0
+    x["k"] = (x["k"].float() * mult[None, None, :, None]).to(torch.bfloat16).contiguous()
+    x = _cuda(x)
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
+    torch.cuda.synchronize()
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    ro, rl = attention_forward(q, k, v, w.scale, causal=causal)
+    assert float(np.max(rl)) * np.log2(np.e) > 128 + 20  # the last jump passes fp32's range
+    _assert_close("O", to_f64(o), ro, BF16_TOL, BF16_REL)
+    _assert_close("LSE", to_f64(lse), rl, LSE_TOL)
+
+
 @pytest.mark.parametrize("waves", ["2", "4"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 37, 64, 100, 200, 257, 777, 1000])

@@ -112,6 +112,73 @@ __device__ __forceinline__ void softmax_tile(f32x16* sacc, float c, int key0, in
   }
 }
 
+// Unmasked key tile of the ping-pong kernel, after the first tile of the
+// range (so the running max m_run is finite): the exponentials are taken
+// against m_run as it stands, without a row max. The running max only has
+// to keep p = 2^(c s - m_run) from overflowing (the shift cancels in o / l),
+// so a block's max is needed only when one of its scores has moved far past
+// m_run, and that shows in the block's sum. Per 32-key block: if any lane's
+// sum of its 16 p exceeds kFastSumLimit (or is inf or NaN), the wave takes
+// the block's max, moves m_run to it, scales o, l and the tile's earlier
+// blocks (sum and bf16 P) by alpha = 2^(m_old - m_new), and redoes the block
+// (scores more than ~20 above the running max in base-2 units: almost never
+// after a row's first tile).
+constexpr float kFastSumLimit = 16777216.0f;  // 2^24
+
+// x * a for the two bf16 halves of a packed word, repacked (round to nearest even).
+__device__ __forceinline__ unsigned scale_bf16x2(unsigned w, float a) {
+  return pack_bf16x2(__uint_as_float(w << 16) * a, __uint_as_float(w & 0xFFFF0000u) * a);
+}
+
+template <int DB, int NKB>
+__device__ __forceinline__ void softmax_tile_running_max(f32x16* sacc, float c, float& m_run,
+                                                         float& l_run, f32x16* oacc, u32x4* pw) {
+  float ls = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = fast_exp2(fmaf(sacc[kb][i], c, -m_run));
+      const float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_run));
+      b0 += p0;
+      b1 += p1;
+      pw[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+    }
+    float bs = b0 + b1;
+    if (__any(!(bs <= kFastSumLimit))) {
+      float mx = sacc[kb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      const float m_new = fmaxf(m_run, max_with_other_half(mx) * c);
+      const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      l_run *= alpha;
+      ls *= alpha;
+#pragma unroll
+      for (int t = 0; t < 2 * kb; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pw[t][e] = scale_bf16x2(pw[t][e], alpha);
+      m_run = m_new;
+      b0 = b1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(fmaf(sacc[kb][i], c, -m_run));
+        const float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_run));
+        b0 += p0;
+        b1 += p1;
+        pw[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+      bs = b0 + b1;
+    }
+    ls += bs;
+  }
+  l_run += ls;
+}
+
 // Value-product steps of an MFMA phase in issue order: the keys of the
 // tile's second half (steps t = NT/2 .. NT-1) first -- their V^T columns were
 // staged by the other group a full phase before the phase starts, so the
@@ -614,8 +681,11 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
       stage_k(tk);
       st.load(krs, vrs, t0 + tk, t0 + tv, r0, gtid);
     }
-    softmax_tile<MASKED, T::DB, T::NKB>(sacc, p.c, kr.k_begin + (j + 1) * BN, kmax, h, m_run, l_run,
+    if (MASKED)
+      softmax_tile<true, T::DB, T::NKB>(sacc, p.c, kr.k_begin + (j + 1) * BN, kmax, h, m_run, l_run,
                                         oacc, pw);
+    else
+      softmax_tile_running_max<T::DB, T::NKB>(sacc, p.c, m_run, l_run, oacc, pw);
     if (!kEarlyLoads) st.store(ks(tk), vs(tv), r0, gtid);
     prefetch_pv<D, BN>(vs(j + 1), vo, pre);
     if (kDirectK) wait_vmem();  // K tile written to LDS
