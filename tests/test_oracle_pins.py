@@ -312,3 +312,47 @@ def test_pins_catch_forward_mutants(mutant):
 def test_pins_catch_backward_mutants(mutant):
     assert _backward_pins_pass(attention_backward)
     assert not _backward_pins_pass(mutant)
+
+
+def test_running_max_reading_stale_reference_gives_the_same_softmax():
+    # The kernels' reading of the running max (design notes, readings table):
+    # any reference value m that keeps 2^(c s - m) finite yields the same O and
+    # LSE, because the shift cancels in o / l. Here, in float64 and base 2 as
+    # the kernels work, m moves only when a 32-key block's sum exceeds 2^24,
+    # and then to that block's max (scaling o, l and the tile's earlier sum by
+    # 2^(m_old - m_new)); rows whose scores jump by ~20 and ~60 mid-sequence
+    # take that path. The result must equal the two-pass definition.
+    rng = np.random.default_rng(31)
+    n, d = 300, 16
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    k[150:] *= 6.0
+    k[230:] *= 4.0
+    v = rng.standard_normal((n, d))
+    scale = 1.0 / np.sqrt(d)
+    c = scale / np.log(2.0)
+    s2 = c * (q @ k.T)  # scores in base-2 units
+    m = s2[:, :32].max(axis=1)  # the first block takes its max, as the kernels' first tile does
+    l = np.zeros(n)
+    o = np.zeros((n, d))
+    moves = 0
+    for b0 in range(0, n, 32):
+        blk = s2[:, b0:b0 + 32]
+        with np.errstate(over="ignore"):
+            p = np.exp2(blk - m[:, None])
+        bs = p.sum(axis=1)
+        if not np.all(bs <= 2.0 ** 24):
+            m_new = np.maximum(m, blk.max(axis=1))
+            alpha = np.exp2(m - m_new)
+            o *= alpha[:, None]
+            l *= alpha
+            m = m_new
+            p = np.exp2(blk - m[:, None])
+            bs = p.sum(axis=1)
+            moves += 1
+        l += bs
+        o += p @ v[b0:b0 + 32]
+    assert moves >= 2  # the jumps did force the max to move
+    ro, rl = attention_forward(q, k, v, scale)
+    np.testing.assert_allclose(o / l[:, None], ro, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose((m + np.log2(l)) * np.log(2.0), rl, rtol=1e-12, atol=1e-12)
