@@ -399,9 +399,10 @@ def test_bwd_ex_small(Nq, Nk, d, causal):
         assert torch.all(dq[:, :, :Nq - Nk] == 0)
 
 
-def test_bwd_ex_empty_sides():
-    q = torch.randn(1, 2, 70, 64, device="cuda").to(torch.bfloat16)
-    kv = torch.randn(1, 2, 90, 64, device="cuda").to(torch.bfloat16)
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_ex_empty_sides(d):
+    q = torch.randn(1, 2, 70, d, device="cuda").to(torch.bfloat16)
+    kv = torch.randn(1, 2, 90, d, device="cuda").to(torch.bfloat16)
     none_q = q[:, :, :0].contiguous()
     none_kv = kv[:, :, :0].contiguous()
     # no query: dK = dV = 0

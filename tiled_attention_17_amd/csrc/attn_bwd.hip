@@ -21,7 +21,9 @@
 //   3. dq:       one workgroup per 256 queries; each wave keeps Q^T and dO^T
 //                of its 32 queries in VGPRs and sweeps the key tiles,
 //                computing S^T = K Q^T and dP^T = V dO^T with the query in
-//                the lane, then dQ^T += K^T dS^T.
+//                the lane, then dQ^T += K^T dS^T; at d = 128 in the
+//                forward's ping-pong schedule (one wave's dS work under the
+//                other's products on each SIMD).
 // Both sweeps run two waves per SIMD and stage tiles with buffer_load ...
 // lds (tile_common.h). The dQ sweep uses the forward's tile shapes: K^T is
 // transposed in registers while staging, so every MFMA operand read is one
@@ -346,35 +348,41 @@ struct DqTile {
   static constexpr int STAGE = 3 * T::KTILE;  // K rows, V rows, K^T
 };
 
-// K^T of one 64-key tile through registers, as the forward stages V^T
-// (Stager's V part: each lane loads the same 8 d-values of two adjacent keys
-// and transpose_v_pair turns them into 8 consecutive keys of two d rows),
-// with one buffer resource per tile (from the tile's first row to the end
-// of the head, so rows past N read as zeros) and per-lane offsets fixed for
-// the whole sweep. The address registers then stay live across the loop: a
-// per-tile offset register, reused by the compiler for a later LDS read while
-// the load was in flight, had the next step's first MFMA wait for the whole
-// staged tile.
-template <int D>
+// K^T of rows [r0, r0 + ROWS) of a 64-key tile through registers, staged
+// by WAVES waves as the forward stages V^T (Stager's V part: each lane loads
+// the same 8 d-values of two adjacent keys and transpose_v_pair turns them
+// into 8 consecutive keys of two d rows), with one buffer resource per tile
+// (from the tile's first row to the end of the head, so rows past N read as
+// zeros) and per-lane offsets fixed for the whole sweep. The address
+// registers then stay live across the loop: a per-tile offset register,
+// reused by the compiler for a later LDS read while the load was in flight,
+// had the next step's first MFMA wait for the whole staged tile. Waves past
+// the last pass load a valid pass again and store nothing (a load under a
+// wave-uniform condition had its registers merged with their old values
+// right after it, a merge that waited for the load).
+template <int D, int WAVES = 8, int ROWS = 64>
 struct KtStager {
   using T = FwdTile<D, 64>;
-  static constexpr int WAVES = 8;
-  static constexpr int VPASS = 64 / T::VKEYS;
+  static constexpr int VPASS = ROWS / T::VKEYS;
   static constexpr int VPW = (VPASS + WAVES - 1) / WAVES;
+  static_assert(ROWS % T::VKEYS == 0, "rows must split into whole passes");
   u32x4 va[VPW], vb[VPW];
-  int wave_;
+  int wave_, r0_;
   int off[VPW];  // byte offset of key kv (and kv + 1 at + 2 D) within a tile
-  // Pass (wave + i * WAVES) of VPASS (at d = 64 only waves 0 .. 3 stage).
+  // Pass (wave + i * WAVES) of VPASS (at d = 64 not every wave stages).
   __device__ __forceinline__ bool has_pass(int i) const {
     return VPASS % WAVES == 0 || wave_ + i * WAVES < VPASS;
   }
-  __device__ __forceinline__ KtStager(int t) {
+  // t: thread index within the staging waves.
+  __device__ __forceinline__ KtStager(int t, int r0 = 0) {
     const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
     wave_ = __builtin_amdgcn_readfirstlane(wave);
+    r0_ = r0;
     const int col = 8 * (r % T::CPR), g = r / T::CPR;
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
-      const int kv = (wave + i * WAVES) * T::VKEYS + 8 * g + 2 * p;
+      const int pass = VPASS % WAVES == 0 ? wave + i * WAVES : min(wave + i * WAVES, VPASS - 1);
+      const int kv = r0 + pass * T::VKEYS + 8 * g + 2 * p;
       off[i] = (kv * D + col) * 2;
     }
   }
@@ -384,25 +392,26 @@ struct KtStager {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kh + (size_t)row0 * D), 0, rem * D * 2, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < VPW; ++i)
-      if (has_pass(i)) {
-        va[i] = buffer_load16(r, off[i]);
-        vb[i] = buffer_load16(r, off[i] + 2 * D);
-      }
+    for (int i = 0; i < VPW; ++i) {
+      va[i] = buffer_load16(r, off[i]);
+      vb[i] = buffer_load16(r, off[i] + 2 * D);
+    }
   }
   __device__ __forceinline__ void store(bf16* kt, int t) const {
-    const int wave = t >> 6, lane = t & 63, p = lane >> 4, r = lane & 15;
+    const int lane = t & 63, p = lane >> 4, r = lane & 15;
     const int d0 = 8 * (r % T::CPR) + 2 * p, g = r / T::CPR;
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
       if (!has_pass(i)) continue;
       u32x4 lo, hi;
       transpose_v_pair(va[i], vb[i], lo, hi);
-      const int slot = (wave + i * WAVES) * T::VKEYS / 8 + g;
+      const int slot = (r0_ + (wave_ + i * WAVES) * T::VKEYS) / 8 + g;
       *(u32x4*)(kt + d0 * 64 + 8 * (slot ^ vt_swz(d0))) = lo;
       *(u32x4*)(kt + (d0 + 1) * 64 + 8 * (slot ^ vt_swz(d0 + 1))) = hi;
     }
   }
+  // Global loads one load() issues (for the scheduling hints).
+  static constexpr int kLoads = 2 * VPW;
 };
 
 template <bool MASKED, int D>
@@ -540,6 +549,227 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
+// 3b. dQ, ping-pong: the sweep above with the forward's ping-pong schedule.
+// The 8 waves form two groups of 4 (one wave of each per SIMD); a wave's
+// work on key tile j is split into an MFMA phase (dQ^T += K^T dS^T of tile j
+// around S^T = K Q^T and dP^T = V dO^T of tile j + 1) and a VALU phase
+// (dS^T of tile j + 1). Group B runs one phase behind group A and every
+// phase ends at a workgroup barrier, so on each SIMD one wave's dS work
+// runs under the other wave's products. K, V rows and K^T are
+// double-buffered; each group stages half of every tile in its VALU phase:
+// group A the K and V rows of tile j + 2 (buffer_load ... lds) and K^T of
+// tile j + 1 (loaded into registers at the start of the MFMA phase, stored
+// transposed in the VALU phase), group B one tile further (j + 3, j + 2),
+// which keeps each buffer free until both groups have read it.
+// ---------------------------------------------------------------------------
+template <int D, int NVMEM = 0, bool DO_S = true, bool DO_PV = true>
+__device__ __forceinline__ void dq_mfma_phase(const bf16* ks, const bf16* vs, const bf16* kt,
+                                              const bf16x8* qf, const bf16x8* dof, const u32x4* pw,
+                                              const VtOffsets& vo, const KOffsets<D, true>& ko,
+                                              const bf16x8* pre, f32x16* sacc, f32x16* dpacc,
+                                              f32x16* dqacc) {
+  using T = FwdTile<D, 64>;
+  constexpr int NPV = DO_PV ? T::NT * T::DB : 0;
+#pragma unroll
+  for (int k = 0; k < NPV / 2; ++k) {
+    const int t = pv_step_t<T::NT>(k, T::DB), db = k % T::DB;
+    const bf16x8 kf = k < kPrefetch ? pre[k] : vt_read<D>(kt, vo, t, db);
+    dqacc[db] = mfma32x32x16(kf, as_bf16x8(pw[t]), dqacc[db]);
+  }
+  if (DO_S) {
+    // four independent chains: S^T and dP^T of both 32-key blocks
+    f32x16 a[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a[x][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < T::DK; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        a[kb] = mfma32x32x16(k_read<D>(ks, ko, s, kb), qf[s], a[kb]);
+        a[2 + kb] = mfma32x32x16(k_read<D>(vs, ko, s, kb), dof[s], a[2 + kb]);
+      }
+    sacc[0] = a[0];
+    sacc[1] = a[1];
+    dpacc[0] = a[2];
+    dpacc[1] = a[3];
+  }
+#pragma unroll
+  for (int k = NPV / 2; k < NPV; ++k) {
+    const int t = pv_step_t<T::NT>(k, T::DB), db = k % T::DB;
+    dqacc[db] = mfma32x32x16(vt_read<D>(kt, vo, t, db), as_bf16x8(pw[t]), dqacc[db]);
+  }
+  // Issue order: global loads, then one LDS read after each MFMA, which
+  // keeps kPrefetch operands in flight.
+  constexpr int NMFMA = NPV + (DO_S ? 4 * T::DK : 0);
+  if (NVMEM > 0) __builtin_amdgcn_sched_group_barrier(0x020, NVMEM, 0);
+  if (!DO_PV) __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + kPrefetch < NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                 const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                                 const float* __restrict__ LSE, const float* __restrict__ Dv,
+                                 bf16* __restrict__ dQ, int Nq, int Nk, int BH, int n_qtiles,
+                                 int total_tiles, float c, float scale, int causal, int remap) {
+  using C = DqTile<D>;
+  using T = typename C::T;
+  using Kt = KtStager<D, 4, 32>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  auto ks = [&](int b) { return smem + (b & 1) * C::STAGE; };
+  auto vs = [&](int b) { return smem + (b & 1) * C::STAGE + T::KTILE; };
+  auto kts = [&](int b) { return smem + (b & 1) * C::STAGE + 2 * T::KTILE; };
+
+  // Tile order as in the lock-step sweep.
+  int bh, qt;
+  if (causal) {
+    const int r = (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x - r * BH;
+    qt = n_qtiles - 1 - r;
+  } else {
+    const int tile = xcd_tile(blockIdx.x, total_tiles, remap);
+    bh = tile / n_qtiles;
+    qt = tile - bh * n_qtiles;
+  }
+  bh = __builtin_amdgcn_readfirstlane(bh);
+  qt = __builtin_amdgcn_readfirstlane(qt);
+  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const bf16* Kh = K + kbase;
+  const bf16* Vh = V + kbase;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;   // 0: group A, 1: group B
+  const int gtid = tid & 255;  // thread index within the group
+  const int r0 = 32 * grp;     // rows of each tile this group stages
+  const int q_row = qt * C::BM + wave * 32 + lq;
+  const bool q_ok = q_row < Nq;
+  const int off = Nk - Nq;
+  const int q_lo = qt * C::BM, q_hi = min(q_lo + C::BM, Nq) - 1;
+  const int lim = causal ? min(Nk, q_hi + off + 1) : Nk;
+  const int n_kt = lim > 0 ? (lim + 63) / 64 : 0;
+  const int all_see = causal ? min(Nk, q_lo + off + 1) : Nk;
+  const int n_full = all_see > 0 ? all_see / 64 : 0;
+  const int kmax = causal ? min(Nk - 1, q_row + off) : Nk - 1;
+
+  f32x16 dqacc[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+  if (n_kt > 0) {  // workgroup-uniform
+    bf16x8 qf[T::DK], dof[T::DK];
+    load_q<D>(Q + qbase + (size_t)q_row * D, q_ok, h, qf);
+    load_q<D>(dO + qbase + (size_t)q_row * D, q_ok, h, dof);
+    // A query that sees no key has LSE = -inf; all its keys are masked.
+    const float lse2 = q_ok ? LSE[(size_t)bh * Nq + q_row] * kLog2e : INFINITY;
+    const float drow = q_ok ? Dv[(size_t)bh * Nq + q_row] : 0.f;
+    const VtOffsets vo(lq, h);
+    const KOffsets<D, true> ko(lq, h);
+    const KDirect<D, 32, 4> kd(r0, wave & 3, lane);
+    Kt st(gtid, r0);
+    auto stage_rows = [&](int t) {  // this group's K and V rows of tile t
+      kd.template load<true>(Kh, Nk, t, 64, ks(t));
+      kd.template load<true>(Vh, Nk, t, 64, vs(t));
+    };
+
+    {  // prologue: everyone stages K, V rows of tiles 0 and 1 and K^T of tile 0
+      const KDirect<D, 64, C::NW> kd0(0, wave, lane);
+      kd0.template load<true>(Kh, Nk, 0, 64, ks(0));
+      kd0.template load<true>(Vh, Nk, 0, 64, vs(0));
+      kd0.template load<true>(Kh, Nk, 1, 64, ks(1));
+      kd0.template load<true>(Vh, Nk, 1, 64, vs(1));
+      KtStager<D> st0(tid);
+      st0.load(Kh, Nk, 0);
+      st0.store(kts(0), tid);
+    }
+    publish_lds();  // also Q^T, dO^T and the row statistics
+    if (grp == 1) phase_barrier();
+
+    f32x16 sacc[2], dpacc[2];
+    u32x4 pw[4];
+    bf16x8 pre[kPrefetch];  // first K^T operands of the next MFMA phase
+
+    // MFMA phase of tile 0: S^T and dP^T only
+    dq_mfma_phase<D, 0, true, false>(ks(0), vs(0), kts(0), qf, dof, pw, vo, ko, pre, sacc, dpacc,
+                                     dqacc);
+    phase_barrier();
+    if (grp == 1) {  // VALU phase "j = -1": group B stages K^T of tile 1, rows of tile 2
+      st.load(Kh, Nk, 1);
+      st.store(kts(1), gtid);
+      stage_rows(2);
+    }
+    if (n_full == 0)
+      dq_scores_to_ds<true, D>(sacc, dpacc, c, lse2, drow, 0, kmax, h, pw);
+    else
+      dq_scores_to_ds<false, D>(sacc, dpacc, c, lse2, drow, 0, kmax, h, pw);
+    prefetch_pv<D, 64>(kts(0), vo, pre);
+    wait_vmem();
+    phase_barrier();
+
+    auto body = [&](auto masked, int j) {
+      constexpr bool MASKED = decltype(masked)::value;
+      const int tr = j + 2 + grp, tt = j + 1 + grp;  // rows / K^T staged here
+      // MFMA phase: dQ^T += K^T dS^T of tile j, S^T and dP^T of tile j + 1.
+      st.load(Kh, Nk, tt);
+      dq_mfma_phase<D, Kt::kLoads>(ks(j + 1), vs(j + 1), kts(j), qf, dof, pw, vo, ko, pre, sacc,
+                                   dpacc, dqacc);
+      phase_barrier();
+      // VALU phase: K^T stores (their loads had the MFMA phase to arrive),
+      // then the row transfers (issued after the stores, so that the
+      // compiler's wait for the K^T loads does not also wait for them),
+      // dS^T of tile j + 1 and the first operands of the next MFMA phase.
+      st.store(kts(tt), gtid);
+      stage_rows(tr);
+      dq_scores_to_ds<MASKED, D>(sacc, dpacc, c, lse2, drow, (j + 1) * 64, kmax, h, pw);
+      prefetch_pv<D, 64>(kts(j + 1), vo, pre);
+      wait_vmem();
+      phase_barrier();
+    };
+    // bodies j = 0 .. n_kt - 2 (body j takes dS of tile j + 1); tiles from
+    // n_full on hold a key some query of the tile may not see.
+    const int n_body = n_kt - 1;
+    const int n_plain = min(max(n_full - 1, 0), n_body);
+    int j = 0;
+    for (; j < n_plain; ++j) body(std::false_type{}, j);
+    for (; j < n_body; ++j) body(std::true_type{}, j);
+    // last tile: dQ product only
+    dq_mfma_phase<D, 0, false>(ks(j + 1), vs(j + 1), kts(j), qf, dof, pw, vo, ko, pre, sacc, dpacc,
+                               dqacc);
+    phase_barrier();
+    phase_barrier();
+    if (grp == 0) phase_barrier();
+  }
+
+  if (q_ok) {
+    bf16* row = dQ + qbase + (size_t)q_row * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dqacc[db][4 * r] * scale, dqacc[db][4 * r + 1] * scale);
+        w[1] = pack_bf16x2(dqacc[db][4 * r + 2] * scale, dqacc[db][4 * r + 3] * scale);
+        *(u32x2*)(row + 32 * db + 8 * r + 4 * h) = w;
+      }
+  }
+}
+
+// The dQ sweep launched for head dimension D (see launch_bwd_d).
+template <int D>
+constexpr auto dq_kernel() {
+  if constexpr (D == 128) return &attn_bwd_dq_pingpong_kernel<D>;
+  else return &attn_bwd_dq_kernel<D>;
+}
+
+// ---------------------------------------------------------------------------
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   const hipStream_t st = (hipStream_t)a.stream;
@@ -574,10 +804,14 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     const int n_qt = (int)((a.Nq + BM - 1) / BM);
     const int64_t total = a.BH * n_qt;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)total), dim3(512), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
-                       a.lse, a.row_dot, (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH, n_qt,
-                       (int)total, c, a.scale, a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
+    // At d = 128 a tile's MFMA phase (48 products) is longer than its dS
+    // phase and the ping-pong sweep overlaps the two; at d = 64 (24
+    // products) the dS work dominates and the lock-step sweep, with half the
+    // barriers, is faster.
+    hipLaunchKernelGGL(dq_kernel<D>(), dim3((unsigned)total), dim3(512), 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, a.lse, a.row_dot,
+                       (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH, n_qt, (int)total, c, a.scale,
+                       a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -179,25 +179,6 @@ __device__ __forceinline__ void softmax_tile_running_max(f32x16* sacc, float c, 
   l_run += ls;
 }
 
-// Value-product steps of an MFMA phase in issue order: the keys of the
-// tile's second half (steps t = NT/2 .. NT-1) first -- their V^T columns were
-// staged by the other group a full phase before the phase starts, so the
-// first operands can be read before the phase's barrier -- then the first
-// half (t = 0 .. NT/2-1).
-template <int NT>
-__device__ __forceinline__ constexpr int pv_step_t(int k, int db_count) {
-  return (k / db_count + NT / 2) % NT;
-}
-constexpr int kPrefetch = 3;  // V^T operand reads issued before the barrier
-
-// First kPrefetch V^T operands of the next MFMA phase (see pv_step_t).
-template <int D, int BN>
-__device__ __forceinline__ void prefetch_pv(const bf16* vt, const VtOffsets& vo, bf16x8* pre) {
-  using T = FwdTile<D, BN>;
-#pragma unroll
-  for (int k = 0; k < kPrefetch; ++k) pre[k] = vt_read<D>(vt, vo, pv_step_t<T::NT>(k, T::DB), k % T::DB);
-}
-
 // One MFMA phase of the ping-pong schedule: O^T += V^T P^T for the current
 // tile (second half of the keys, then first half) around S^T = K Q^T for
 // the next tile (NKB independent chains that alternate, so that none waits

@@ -164,6 +164,26 @@ __device__ __forceinline__ void pv_tile(const bf16* vt, const u32x4* pw, const V
   interleave_lds_mfma<4 * T::DB>();
 }
 
+// Value-product steps of a ping-pong MFMA phase (the forward's O^T += V^T P^T,
+// the dQ sweep's dQ^T += K^T dS^T) in issue order: the keys of the tile's
+// second half (steps t = NT/2 .. NT-1) first -- their V^T columns were
+// staged by the other group a full phase before the phase starts, so the
+// first operands can be read before the phase's barrier -- then the first
+// half (t = 0 .. NT/2-1).
+template <int NT>
+__device__ __forceinline__ constexpr int pv_step_t(int k, int db_count) {
+  return (k / db_count + NT / 2) % NT;
+}
+constexpr int kPrefetch = 3;  // V^T operand reads issued before the barrier
+
+// First kPrefetch V^T operands of the next MFMA phase (see pv_step_t).
+template <int D, int BN>
+__device__ __forceinline__ void prefetch_pv(const bf16* vt, const VtOffsets& vo, bf16x8* pre) {
+  using T = FwdTile<D, BN>;
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) pre[k] = vt_read<D>(vt, vo, pv_step_t<T::NT>(k, T::DB), k % T::DB);
+}
+
 // Q^T as the B operand: lane (query lq, half h) holds d = 16 s + 8 h .. +7.
 template <int D>
 __device__ __forceinline__ void load_q(const bf16* qrow, bool q_ok, int h, bf16x8* qf) {
