@@ -5,7 +5,9 @@ built with TATTN_ORDERED_LDS_DMA: every LDS transfer the kernels order by
 hand goes through the form the compiler orders, with an extra wait and
 barrier where a staged tile is published. It is a debug build for parity
 runs (the binding loads it when TILED_ATTN_LIBRARY=ordered), never the
-measured one.
+measured one. libtattn_probe.so is a measurement probe of the chip's
+sustained matrix-core rate (profiling.py mfma-ceiling), apart from the
+attention path.
 """
 
 from __future__ import annotations
@@ -19,6 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtiledattn.so")
 LIB_ORDERED = os.path.join(PKG, "libtiledattn_ordered.so")
+# measurement probe (profiling.py mfma-ceiling), never loaded by the attention path
+LIB_PROBE = os.path.join(PKG, "libtattn_probe.so")
+PROBE_SOURCES = ["mfma_ceiling.hip"]
 SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "matmul.hip", "attn_fp8.hip"]
 
 FLAGS = [
@@ -34,13 +39,14 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, ordered_lds_dma: bool = False) -> str:
+def build(verbose: bool = False, ordered_lds_dma: bool = False, probe: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    out = LIB_ORDERED if ordered_lds_dma else LIB
+    out = LIB_PROBE if probe else (LIB_ORDERED if ordered_lds_dma else LIB)
     tmp = out + ".tmp"
     defs = ["-DTATTN_ORDERED_LDS_DMA"] if ordered_lds_dma else []
+    sources = PROBE_SOURCES if probe else SOURCES
     cmd = [hipcc, *FLAGS, *defs, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,4 +61,5 @@ def build(verbose: bool = False, ordered_lds_dma: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, ordered_lds_dma="--ordered-lds-dma" in sys.argv))
+    print(build(verbose="-v" in sys.argv, ordered_lds_dma="--ordered-lds-dma" in sys.argv,
+                probe="--probe" in sys.argv))

@@ -32,6 +32,13 @@
       settle_launches + warmup untimed launches, then `steps` timed ones),
       with their average duration and roofline fraction beside the line's.
 
+  python -m tiled_attention_17_amd.profiling mfma-ceiling [--iters 1200] [--settle-ms 500] [--out-md FILE]
+      Runs the matrix-core probe (libtattn_probe.so, csrc/mfma_ceiling.hip)
+      in each of its modes on every CU, after a clock settle per mode, and
+      writes a table of sustained bf16 TFLOP/s and shader clock: constant
+      against random operands, with LDS operand reads and the softmax's
+      vector work added, and the 16x16x32 shape.
+
   python -m tiled_attention_17_amd.profiling summarize --fetch DIR --write DIR [--stats DIR]
       Reads the counter CSVs of the two runs (FETCH_SIZE, WRITE_SIZE; KiB per
       dispatch), scales the forward kernel's figures by what the same counter
@@ -396,6 +403,96 @@ def summarize_bench(trace_dir, bench_line, cmd, out_md):
     print("\n".join(lines[:20]))
 
 
+PROBE_MODES = [
+    (0, "32x32x16, constant operands"),
+    (1, "32x32x16, random operands"),
+    (3, "32x32x16, random, A read from LDS"),
+    (5, "32x32x16, random, + one softmax element per MFMA"),
+    (7, "32x32x16, random, LDS A + softmax element"),
+    (9, "16x16x32 (two per unit), random operands"),
+    (15, "16x16x32, random, LDS A + softmax element"),
+    (19, "LDS reads alone (no MFMA)"),
+    (21, "softmax elements alone (no MFMA)"),
+]
+
+
+def mfma_ceiling(iters, settle_ms, out_md, command):
+    """Sustained matrix-core rate and shader clock per probe mode (see csrc/mfma_ceiling.hip)."""
+    import ctypes
+    import time
+
+    import torch
+
+    from tiled_attention_17_amd.build import LIB_PROBE
+
+    if not os.path.exists(LIB_PROBE):
+        raise RuntimeError(f"{LIB_PROBE} is not built (tiled_attention_17_amd/build.py --probe)")
+    lib = ctypes.CDLL(LIB_PROBE)
+    lib.tattn_probe_mfma_ceiling.restype = ctypes.c_int
+    lib.tattn_probe_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(0)
+    grid = props.multi_processor_count
+    out = torch.zeros(grid * 8 * 2, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(grid * 512, dtype=torch.float32, device="cuda")
+    g = torch.Generator().manual_seed(1)
+    rnd_vecs = grid * 512 * 16
+    rnd = torch.randn(rnd_vecs * 8, generator=g).to(torch.bfloat16).cuda()  # N(0, 1) bf16, 8 per 16-byte word
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch(mode):
+        r = lib.tattn_probe_mfma_ceiling(mode, out.data_ptr(), sink.data_ptr(), rnd.data_ptr(), rnd_vecs, grid,
+                                         iters, st)
+        if r != 0:
+            raise RuntimeError(f"probe mode {mode}: status {r}")
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rows = []
+    for mode, desc in PROBE_MODES:
+        t_end = time.time() + settle_ms / 1e3
+        while time.time() < t_end:
+            for _ in range(10):
+                launch(mode)
+            torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(10):
+            launch(mode)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / 10 * 1e3
+        o = out.view(-1, 2).cpu().double()
+        clock = (o[:, 0] / o[:, 1]).median().item() * 0.1  # shader ticks per 100 MHz tick -> GHz
+        tf = 0.0 if mode & 16 else grid * 8 * iters * 8 * 32768 / (us * 1e-6) / 1e12
+        rows.append((mode, desc, us, clock, tf))
+        print(f"mode {mode:2d} {desc:48s} {us:8.1f} us  clock {clock:5.2f} GHz  {tf:7.1f} TFLOP/s", flush=True)
+    lines = [
+        "# Sustained bf16 matrix-core rate and shader clock (one MI355X)",
+        "",
+        "Measurement probe `tiled_attention_17_amd/csrc/mfma_ceiling.hip` (library `libtattn_probe.so`), one",
+        f"512-thread workgroup on each of the {grid} CUs, two waves per SIMD, {iters} iterations of 8 units of",
+        "32768 FLOPs per wave, each mode after a clock settle of "
+        f"{settle_ms} ms; time from HIP events over 10 launches, clock",
+        "from the waves' `s_memtime` / `s_memrealtime` ticks. Random operands are N(0, 1) in bf16, as the",
+        "attention workloads' inputs; the softmax element is one FMA, one exp2, one add and half a bf16 pack.",
+        "The LDS modes keep two operand reads in flight per wave, so part of their drop is read latency;",
+        "their clocks show what the reads add to the power.",
+        "",
+        "Command (repo root on the box):",
+        "",
+        f"    {command}",
+        "",
+        "| mode | work | us per launch | clock GHz | TFLOP/s | % of 2.5 PFLOP/s |",
+        "|---|---|---|---|---|---|",
+    ]
+    for mode, desc, us, clock, tf in rows:
+        pct = f"{tf / 2500 * 100:.1f} %" if tf else "-"
+        tfs = f"{tf:.0f}" if tf else "-"
+        lines.append(f"| {mode} | {desc} | {us:.1f} | {clock:.2f} | {tfs} | {pct} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote", out_md)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -416,6 +513,11 @@ def main():
     sb.add_argument("--bench-line", required=True)
     sb.add_argument("--command", required=True)
     sb.add_argument("--out-md", default=os.path.join(ROOT, "profiles", "fwd_bf16_n4096_d128_kernel_stats.md"))
+    mc = sub.add_parser("mfma-ceiling")
+    mc.add_argument("--iters", type=int, default=1200)
+    mc.add_argument("--settle-ms", type=int, default=500)
+    mc.add_argument("--out-md", default=os.path.join(ROOT, "profiles", "mfma_ceiling_bf16.md"))
+    mc.add_argument("--command", default="python3 -m tiled_attention_17_amd.profiling mfma-ceiling")
     s = sub.add_parser("summarize")
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
@@ -430,6 +532,8 @@ def main():
         run_set(a.launches, a.copy_mib)
     elif a.cmd == "summarize-bench":
         summarize_bench(a.trace, a.bench_line, a.command, a.out_md)
+    elif a.cmd == "mfma-ceiling":
+        mfma_ceiling(a.iters, a.settle_ms, a.out_md, a.command)
     elif a.cmd == "summarize-set":
         summarize_set(a.sq, a.fetch, a.write, a.copy_mib, a.out_md)
     else:
