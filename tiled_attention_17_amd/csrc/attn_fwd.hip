@@ -550,10 +550,12 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
 // every phase ends at a workgroup barrier, so on each SIMD one wave feeds
 // the matrix core while the other wave computes exponentials: a wave's own
 // VALU work does not overlap its own MFMAs, but another wave's does.
-// K and V tiles are double-buffered; each group stages half of every tile
-// during its VALU phase (group A: K_{j+2}, V_{j+1}; group B, one phase later
-// in time but one tile ahead: K_{j+3}, V_{j+2}), which keeps each buffer
-// free until both groups have read it.
+// K and V tiles are double-buffered; each group stages half of every V tile
+// during its VALU phase (group A: V_{j+1}; group B, one phase later in time
+// but one tile ahead: V_{j+2}), which keeps each buffer free until both
+// groups have read it. 128-key K tiles go straight to LDS, sent whole by
+// group A at the start of its MFMA phase j (K_{j+2}); 64-key K tiles go
+// through registers, half by each group (K_{j+2}, K_{j+3}).
 // ---------------------------------------------------------------------------
 template <int D, int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -596,9 +598,15 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
   const int kmax = row_kmax(p, kr, q_row);
   const VtOffsets vo(lq, h);
   const KOffsets<D> ko(lq, h);
-  const KDirect<D, BN / 2> kd(r0, wave & 3, lane);
-  auto stage_k = [&](int t) {  // this group's rows of local K tile t (direct mode)
-    if (kDirectK) kd.load(Kh, p.Nk, t0 + t, BN, ks(t));
+  // With K staged straight into LDS (128-key tiles), group A sends the whole
+  // of K_{j+2} at the start of its MFMA phase j: that buffer's last reader,
+  // group B's MFMA phase j-1, is done, the phase itself reads only K_{j+1}
+  // and V, and the transfer is waited for at the end of A's VALU phase j, a
+  // phase before group A reads the tile. The transfers' issue time then
+  // falls in the shorter MFMA phase instead of both groups' VALU phases.
+  const KDirect<D, BN, 4> kda(0, wave & 3, lane);
+  auto stage_k = [&](int t) {  // local K tile t, by group A (direct mode)
+    if (kDirectK && grp == 0) kda.template load<true>(Kh, p.Nk, t0 + t, BN, ks(t));
   };
 
   bf16x8 qf[T::DK];
@@ -625,7 +633,8 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
   f32x16 sacc[T::NKB];
   u32x4 pw[T::NT];
   bf16x8 pre[kPrefetch];  // first V^T operands of the next MFMA phase
-  // Group A stages (K_{j+2}, V_{j+1}) in VALU phase j, group B (K_{j+3}, V_{j+2}).
+  // Group A stages V_{j+1} in VALU phase j, group B V_{j+2} (and K through
+  // registers, 64-key tiles: K_{j+2} and K_{j+3}).
   // Tiles past the end of the head are zero-filled without memory traffic;
   // tiles past the end of the range go into buffers no wave reads any more.
   StG st;
@@ -633,10 +642,7 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
   // MFMA phase of tile 0: scores only
   mfma_phase<D, BN, 0, true, false>(ks(0), vs(0), qf, pw, vo, ko, pre, sacc, oacc);
   phase_barrier();
-  if (grp == 1) {  // VALU phase "j = -1"
-    stage_k(2);
-    st.load(krs, vrs, t0 + 2, t0 + 1, r0, gtid);
-  }
+  if (grp == 1) st.load(krs, vrs, t0 + 2, t0 + 1, r0, gtid);  // VALU phase "j = -1"
   if (kr.n_full == 0)
     softmax_tile<true, T::DB, T::NKB>(sacc, p.c, kr.k_begin, kmax, h, m_run, l_run, oacc, pw);
   else
@@ -651,6 +657,7 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
     // MFMA phase: O^T += V^T P^T of tile j, S^T of tile j+1.
     const int tk = j + 2 + grp, tv = j + 1 + grp;
     if (kEarlyLoads) st.load(krs, vrs, t0 + tk, t0 + tv, r0, gtid);
+    stage_k(j + 2);
     mfma_phase<D, BN, kEarlyLoads ? NVMEM : 0>(ks(j + 1), vs(j), qf, pw, vo, ko, pre, sacc, oacc);
     phase_barrier();
     // VALU phase: staging of later tiles (with early loads first, so that
@@ -659,7 +666,6 @@ void attn_fwd_bf16_pingpong_kernel(const FwdParams p) {
     if (kEarlyLoads) {
       st.store(ks(tk), vs(tv), r0, gtid);
     } else {
-      stage_k(tk);
       st.load(krs, vrs, t0 + tk, t0 + tv, r0, gtid);
     }
     if (MASKED)
