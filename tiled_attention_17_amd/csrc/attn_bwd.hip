@@ -357,9 +357,7 @@ struct DqTile {
 // registers then stay live across the loop: a per-tile offset register,
 // reused by the compiler for a later LDS read while the load was in flight,
 // had the next step's first MFMA wait for the whole staged tile. Waves past
-// the last pass load a valid pass again and store nothing (a load under a
-// wave-uniform condition had its registers merged with their old values
-// right after it, a merge that waited for the load).
+// the last pass (at d = 64) load and store nothing.
 template <int D, int WAVES = 8, int ROWS = 64>
 struct KtStager {
   using T = FwdTile<D, 64>;
@@ -381,8 +379,7 @@ struct KtStager {
     const int col = 8 * (r % T::CPR), g = r / T::CPR;
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
-      const int pass = VPASS % WAVES == 0 ? wave + i * WAVES : min(wave + i * WAVES, VPASS - 1);
-      const int kv = r0 + pass * T::VKEYS + 8 * g + 2 * p;
+      const int kv = r0 + (wave + i * WAVES) * T::VKEYS + 8 * g + 2 * p;
       off[i] = (kv * D + col) * 2;
     }
   }
@@ -392,10 +389,11 @@ struct KtStager {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kh + (size_t)row0 * D), 0, rem * D * 2, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-      va[i] = buffer_load16(r, off[i]);
-      vb[i] = buffer_load16(r, off[i] + 2 * D);
-    }
+    for (int i = 0; i < VPW; ++i)
+      if (has_pass(i)) {
+        va[i] = buffer_load16(r, off[i]);
+        vb[i] = buffer_load16(r, off[i] + 2 * D);
+      }
   }
   __device__ __forceinline__ void store(bf16* kt, int t) const {
     const int lane = t & 63, p = lane >> 4, r = lane & 15;
