@@ -42,6 +42,26 @@ def _wl(B, H, Nq, Nk, d, dtype="bf16", seed=0, q_std=1.0, causal=False):
                     n_k=Nk, causal=causal)
 
 
+BF16_U = 2.0 ** -8  # unit roundoff of bf16 round-to-nearest-even (8 significant bits)
+
+
+def _assert_grad(name, got, want):
+    """A gradient within 2e-2 + 2u max|ref| (one u for the rounding of the
+    result to bf16, one for the bf16 rounding of the P and dS operands), and
+    within 2e-2 max|ref| + 1e-4 (a wrongly scaled result fails). Needed where
+    gradients grow past ~2: under the mask with N_q > N_k the first visible
+    query sees one key with P = 1, and that key's dV sums dO rows with
+    weights 1, 1/2, 1/3, ..."""
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    if not want.size:
+        return
+    err = float(np.max(np.abs(got - want)))
+    scale = float(np.max(np.abs(want)))
+    bound = BF16_TOL + 2 * BF16_U * scale
+    assert err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e} (max|ref| {scale:.3e})"
+    assert err <= BF16_REL * scale + 1e-4, f"{name}: max err {err:.3e} > {BF16_REL} * max|ref| {scale:.3e} + 1e-4"
+
+
 def _assert_o(name, got, want, tol, rel):
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     err = float(np.max(np.abs(got - want))) if want.size else 0.0
@@ -432,3 +452,44 @@ def test_workload_causal_fwd_bwd_every_head():
         got = to_f64(got)
         for (b, h) in np.ndindex(w.B, w.H):
             _assert_o(f"{name}[{b},{h}]", got[b, h], want[b, h], BF16_TOL, BF16_REL)
+
+
+# ---------------------------------------------------------------------------
+# size extremes: a long sequence and a grid of many small heads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_fwd_bwd_whole(causal):
+    # One head of 16384 queries and keys (four times the forward + backward
+    # workload's length, 64 query tiles and 64 key tiles per sweep): every
+    # element of O, LSE, dQ, dK and dV against the oracle.
+    w = _wl(1, 1, 16384, 16384, 128, seed=77 + int(causal), causal=causal)
+    x = _cuda(make_inputs(w, with_grad_output=True))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
+    dq, dk, dv = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=causal)
+    torch.cuda.synchronize()
+    _check_whole(x, o, lse, w.scale, causal)
+    _check_bwd(x, dq, dk, dv, w.scale, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads_fwd_bwd_whole(d, causal):
+    # 8 x 64 = 512 heads of 80 queries against 72 keys: thousands of small,
+    # ragged tiles (head decoding and the XCD remap across a large grid; with
+    # the mask the first 8 queries of every head see no key).
+    w = _wl(8, 64, 80, 72, d, seed=300 + d + int(causal), causal=causal)
+    x = _cuda(make_inputs(w, with_grad_output=True))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
+    dq, dk, dv = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=causal)
+    torch.cuda.synchronize()
+    _check_whole(x, o, lse, w.scale, causal)
+    q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    ref = backward_all(q, k, v, do, w.scale, causal=causal)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        got = to_f64(got)
+        for (b, h) in np.ndindex(w.B, w.H):
+            _assert_grad(f"{name}[{b},{h}]", got[b, h], want[b, h])
+    if causal:
+        assert torch.all(dq[:, :, :8] == 0)
