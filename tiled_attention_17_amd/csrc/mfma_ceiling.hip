@@ -16,7 +16,11 @@
 //      contents, conflict-free), as the attention kernels read K and V^T;
 //   4  one softmax-like element per unit (fma, exp2, add, half a bf16 pack),
 //      the forward's vector work per MFMA;
-//   16 no matrix work (the other work alone).
+//   16 no matrix work (the other work alone);
+//   32 each group of four consecutive MFMAs shares one B operand;
+//   64 each group of four consecutive MFMAs shares one A operand
+//      (32 and 64: how much of the power follows operand changes from one
+//      MFMA to the next).
 // Lane 0 of each wave writes the s_memtime (shader clock) and
 // s_memrealtime (100 MHz) ticks around its loop; their ratio is the clock.
 #include <hip/hip_runtime.h>
@@ -82,11 +86,13 @@ void mfma_ceiling_kernel(unsigned long long* out, float* sink, int iters, const 
       if (!(MODE & 16)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const bf16x8 ai = (MODE & 64) ? a[0] : a[i];
+          const bf16x8 bi = (MODE & 32) ? rb[4 * u] : rb[4 * u + i];
           if (MODE & 8) {
-            e[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], rb[4 * u + i], e[2 * i], 0, 0, 0);
-            e[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[4 * u + i], a[i], e[2 * i + 1], 0, 0, 0);
+            e[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, bi, e[2 * i], 0, 0, 0);
+            e[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bi, ai, e[2 * i + 1], 0, 0, 0);
           } else {
-            c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], rb[4 * u + i], c[i], 0, 0, 0);
+            c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ai, bi, c[i], 0, 0, 0);
           }
         }
       } else if (MODE & 2) {
@@ -156,6 +162,9 @@ int tattn_probe_mfma_ceiling(int mode, void* out, void* sink, const void* rnd, i
     case 15: e = launch<15>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
     case 19: e = launch<19>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
     case 21: e = launch<21>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
+    case 33: e = launch<33>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
+    case 65: e = launch<65>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
+    case 97: e = launch<97>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
     default: return 1;
   }
   return e == hipSuccess ? 0 : 2;

@@ -413,6 +413,9 @@ PROBE_MODES = [
     (15, "16x16x32, random, LDS A + softmax element"),
     (19, "LDS reads alone (no MFMA)"),
     (21, "softmax elements alone (no MFMA)"),
+    (33, "32x32x16, random, B shared by 4 consecutive MFMAs"),
+    (65, "32x32x16, random, A shared by 4 consecutive MFMAs"),
+    (97, "32x32x16, random, A and B shared by 4 consecutive MFMAs"),
 ]
 
 
