@@ -20,7 +20,9 @@
 //   32 each group of four consecutive MFMAs shares one B operand;
 //   64 each group of four consecutive MFMAs shares one A operand
 //      (32 and 64: how much of the power follows operand changes from one
-//      MFMA to the next).
+//      MFMA to the next; with 2, one LDS read per four MFMAs);
+//   128 each pair of consecutive MFMAs shares one A operand (with 2, one
+//      LDS read per two MFMAs, as a wave of 64 queries would read K and V^T).
 // Lane 0 of each wave writes the s_memtime (shader clock) and
 // s_memrealtime (100 MHz) ticks around its loop; their ratio is the clock.
 #include <hip/hip_runtime.h>
@@ -86,7 +88,7 @@ void mfma_ceiling_kernel(unsigned long long* out, float* sink, int iters, const 
       if (!(MODE & 16)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bf16x8 ai = (MODE & 64) ? a[0] : a[i];
+          const bf16x8 ai = (MODE & 64) ? a[0] : (MODE & 128) ? a[i & 2] : a[i];
           const bf16x8 bi = (MODE & 32) ? rb[4 * u] : rb[4 * u + i];
           if (MODE & 8) {
             e[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, bi, e[2 * i], 0, 0, 0);
@@ -165,6 +167,9 @@ int tattn_probe_mfma_ceiling(int mode, void* out, void* sink, const void* rnd, i
     case 33: e = launch<33>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
     case 65: e = launch<65>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
     case 97: e = launch<97>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
+    case 71: e = launch<71>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
+    case 129: e = launch<129>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
+    case 135: e = launch<135>(out, sink, rnd, rnd_vecs, grid, iters, st); break;
     default: return 1;
   }
   return e == hipSuccess ? 0 : 2;

@@ -416,6 +416,9 @@ PROBE_MODES = [
     (33, "32x32x16, random, B shared by 4 consecutive MFMAs"),
     (65, "32x32x16, random, A shared by 4 consecutive MFMAs"),
     (97, "32x32x16, random, A and B shared by 4 consecutive MFMAs"),
+    (129, "32x32x16, random, A shared by 2 consecutive MFMAs"),
+    (135, "32x32x16, random, LDS A read per 2 MFMAs + softmax element"),
+    (71, "32x32x16, random, LDS A read per 4 MFMAs + softmax element"),
 ]
 
 
