@@ -8,8 +8,15 @@
 //   P = exp(scale S - LSE), dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i,
 //   dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
-// Three launches on the caller's stream, no atomics (deterministic):
-//   1. row_dot:  D_i = sum_k dO_ik O_ik (memory-bound, one pass over O, dO);
+// Two launches on the caller's stream, no atomics (deterministic):
+//   1. dq:       one workgroup per 256 queries; each wave keeps Q^T and dO^T
+//                of its 32 queries in VGPRs, first forms the row terms
+//                D_i = sum_k dO_ik O_ik of its queries (and writes them for
+//                the second launch), then sweeps the key tiles, computing
+//                S^T = K Q^T and dP^T = V dO^T with the query in the lane,
+//                then dQ^T += K^T dS^T; at d = 128 in the forward's ping-pong
+//                schedule (one wave's dS work under the other's products on
+//                each SIMD);
 //   2. dkdv:     one workgroup per 256 keys; each wave keeps K^T of its 32
 //                keys in VGPRs, the workgroup keeps the V rows of its keys
 //                in LDS, and the query tiles stream through LDS (64 queries
@@ -17,13 +24,7 @@
 //                dP = dO V^T with the key in the lane so that P and dS feed
 //                dV^T += dO^T P and dK^T += Q^T dS as B operands; dO^T and
 //                Q^T come from ds_read_b64_tr_b16 transposed reads of the
-//                row-major tiles;
-//   3. dq:       one workgroup per 256 queries; each wave keeps Q^T and dO^T
-//                of its 32 queries in VGPRs and sweeps the key tiles,
-//                computing S^T = K Q^T and dP^T = V dO^T with the query in
-//                the lane, then dQ^T += K^T dS^T; at d = 128 in the
-//                forward's ping-pong schedule (one wave's dS work under the
-//                other's products on each SIMD).
+//                row-major tiles.
 // Both sweeps run two waves per SIMD and stage tiles with buffer_load ...
 // lds (tile_common.h). The dQ sweep uses the forward's tile shapes: K^T is
 // transposed in registers while staging, so every MFMA operand read is one
@@ -43,30 +44,6 @@
 namespace tattn {
 
 
-
-// ---------------------------------------------------------------------------
-// 1. D_i = dO_i . O_i
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_rowdot_kernel(const bf16* __restrict__ O,
-                                                              const bf16* __restrict__ dO,
-                                                              float* __restrict__ Dv,
-                                                              int64_t rows) {
-  constexpr int TPR = D / 8;  // threads per row, 8 elements (16 bytes) each
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
-  const int part = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    u32x4 a = *(const u32x4*)(O + row * D + part * 8);
-    u32x4 b = *(const u32x4*)(dO + row * D + part * 8);
-    bf16x8 x = as_bf16x8(a), y = as_bf16x8(b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) Dv[row] = acc;
-}
 
 // ---------------------------------------------------------------------------
 // 2. dK, dV
@@ -340,6 +317,27 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 //                                     transpose; read with ds_read_b128)
 // so every MFMA operand read is one ds_read_b128 and no transposed LDS read
 // is needed. dQ = scale dQ^T^T at the end.
+// The row term D_i = dO_i . O_i of dS for the query this lane owns: the lane
+// holds the dO values of its half of the row (the layout of load_q), takes
+// the matching O values and adds the other half's partial sum. Lanes of the
+// first half write it to drow_out for the dK/dV sweep, which runs after this
+// one; every query row gets its term, also one that sees no key (the dK/dV
+// sweep multiplies its masked pairs' zero P by it).
+template <int D>
+__device__ __forceinline__ float row_term(const bf16* orow, const bf16x8* dof, bool q_ok, int h,
+                                          float* drow_out) {
+  bf16x8 of[D / 16];
+  load_q<D>(orow, q_ok, h, of);
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)of[s][e], (float)dof[s][e], acc);
+  const float d = add_other_half(acc);
+  if (q_ok && h == 0) *drow_out = d;
+  return d;
+}
+
 template <int D>
 struct DqTile {
   static constexpr int NW = 8;
@@ -436,8 +434,9 @@ __device__ __forceinline__ void dq_scores_to_ds(const f32x16* sacc, const f32x16
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                        const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                        const float* __restrict__ LSE, const float* __restrict__ Dv,
+                        const bf16* __restrict__ V, const bf16* __restrict__ O,
+                        const bf16* __restrict__ dO, const float* __restrict__ LSE,
+                        float* __restrict__ Dv,
                         bf16* __restrict__ dQ, int Nq, int Nk, int BH, int n_qtiles, int total_tiles,
                         float c, float scale, int causal, int remap) {
   using C = DqTile<D>;
@@ -483,7 +482,7 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   load_q<D>(dO + qbase + (size_t)q_row * D, q_ok, h, dof);
   // A query that sees no key has LSE = -inf; all its keys are masked.
   const float lse2 = q_ok ? LSE[(size_t)bh * Nq + q_row] * kLog2e : INFINITY;
-  const float drow = q_ok ? Dv[(size_t)bh * Nq + q_row] : 0.f;
+  const float drow = row_term<D>(O + qbase + (size_t)q_row * D, dof, q_ok, h, Dv + (size_t)bh * Nq + q_row);
 
   const VtOffsets vo(lq, h);
   const KOffsets<D, true> ko(lq, h);
@@ -613,8 +612,9 @@ __device__ __forceinline__ void dq_mfma_phase(const bf16* ks, const bf16* vs, co
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                                 const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                                 const float* __restrict__ LSE, const float* __restrict__ Dv,
+                                 const bf16* __restrict__ V, const bf16* __restrict__ O,
+                                 const bf16* __restrict__ dO, const float* __restrict__ LSE,
+                                 float* __restrict__ Dv,
                                  bf16* __restrict__ dQ, int Nq, int Nk, int BH, int n_qtiles,
                                  int total_tiles, float c, float scale, int causal, int remap) {
   using C = DqTile<D>;
@@ -662,13 +662,14 @@ void attn_bwd_dq_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restr
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
+  bf16x8 dof[T::DK];
+  load_q<D>(dO + qbase + (size_t)q_row * D, q_ok, h, dof);
+  const float drow = row_term<D>(O + qbase + (size_t)q_row * D, dof, q_ok, h, Dv + (size_t)bh * Nq + q_row);
   if (n_kt > 0) {  // workgroup-uniform
-    bf16x8 qf[T::DK], dof[T::DK];
+    bf16x8 qf[T::DK];
     load_q<D>(Q + qbase + (size_t)q_row * D, q_ok, h, qf);
-    load_q<D>(dO + qbase + (size_t)q_row * D, q_ok, h, dof);
     // A query that sees no key has LSE = -inf; all its keys are masked.
     const float lse2 = q_ok ? LSE[(size_t)bh * Nq + q_row] * kLog2e : INFINITY;
-    const float drow = q_ok ? Dv[(size_t)bh * Nq + q_row] : 0.f;
     const VtOffsets vo(lq, h);
     const KOffsets<D, true> ko(lq, h);
     const KDirect<D, 32, 4> kd(r0, wave & 3, lane);
@@ -772,15 +773,24 @@ template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   const hipStream_t st = (hipStream_t)a.stream;
   const float c = a.scale * kLog2e;
-  // With no query, the dK/dV kernel alone runs (it writes zeros); with no
-  // key, the dQ kernel alone runs (likewise).
+  // The dQ sweep runs first: it also writes the row terms D_i that the
+  // dK/dV sweep reads. With no query, the dK/dV kernel alone runs (it writes
+  // zeros and reads no row term); with no key, the dQ kernel alone runs
+  // (likewise).
   const int64_t rows = a.BH * a.Nq;
   if (rows > 0) {
-    constexpr int rows_per_block = 256 / (D / 8);
-    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-    if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bwd_rowdot_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const bf16*)a.o, (const bf16*)a.dout, a.row_dot, rows);
+    constexpr int BM = DqTile<D>::BM;
+    const int n_qt = (int)((a.Nq + BM - 1) / BM);
+    const int64_t total = a.BH * n_qt;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    // At d = 128 a tile's MFMA phase (48 products) is longer than its dS
+    // phase and the ping-pong sweep overlaps the two; at d = 64 (24
+    // products) the dS work dominates and the lock-step sweep, with half the
+    // barriers, is faster.
+    hipLaunchKernelGGL(dq_kernel<D>(), dim3((unsigned)total), dim3(512), 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o, (const bf16*)a.dout, a.lse,
+                       a.row_dot, (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH, n_qt, (int)total, c,
+                       a.scale, a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -797,22 +807,6 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (rows > 0) {
-    constexpr int BM = DqTile<D>::BM;
-    const int n_qt = (int)((a.Nq + BM - 1) / BM);
-    const int64_t total = a.BH * n_qt;
-    if (total > INT32_MAX) return hipErrorInvalidValue;
-    // At d = 128 a tile's MFMA phase (48 products) is longer than its dS
-    // phase and the ping-pong sweep overlaps the two; at d = 64 (24
-    // products) the dS work dominates and the lock-step sweep, with half the
-    // barriers, is faster.
-    hipLaunchKernelGGL(dq_kernel<D>(), dim3((unsigned)total), dim3(512), 0, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout, a.lse, a.row_dot,
-                       (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH, n_qt, (int)total, c, a.scale,
-                       a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   return hipSuccess;
 }
 
@@ -825,8 +819,8 @@ hipError_t launch_attn_bwd(const BwdArgs& a) {
 // uses) go to this fixed device array. Each device holds its own copy, at
 // its own address; in host code the name is only a stand-in for the symbol,
 // so kernels get the device address hipGetSymbolAddress reports, looked up
-// once per device (with that device current) and kept. The row-dot kernel
-// writes every D_i a call reads before the sweeps read it, so nothing needs
+// once per device (with that device current) and kept. The dQ sweep writes
+// every D_i a call reads before the dK/dV sweep reads it, so nothing needs
 // clearing between calls; calls that overlap on one device share the array
 // and race.
 // ---------------------------------------------------------------------------

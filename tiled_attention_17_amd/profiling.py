@@ -245,8 +245,7 @@ def summarize_set(sq_dir, fetch_dir, write_dir, copy_mib, out_md):
               "its measured rate; the bf16 kernels' LDS layouts (swizzled K, V^T, Q/dO tiles and their",
               "transposed reads) show no bank-conflict cycles (the one-query kernel's LDS traffic is its",
               "cross-lane shuffles and the end-of-sweep merge of its waves, once per workgroup); HBM bytes",
-              "of the headline forward match its algorithmic bytes, and decode and the row-dot kernel run",
-              "near the HBM rate."]
+              "of the headline forward match its algorithmic bytes, and decode runs near the HBM rate."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
