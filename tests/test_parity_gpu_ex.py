@@ -420,6 +420,27 @@ def test_bwd_ex_small(Nq, Nk, d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ex_ignores_stale_workspace(d, causal):
+    # The workspace holds the row terms D_i; its contents on entry are ignored:
+    # every term the dK/dV sweep reads (also for queries that see no key, whose
+    # zero P it multiplies) is written earlier in the same call. A workspace
+    # full of NaN must give the same gradients, bit for bit, as a zeroed one.
+    w = _wl(1, 3, 777, 300, d, seed=90 + d + causal)
+    x = _cuda(make_inputs(w, with_grad_output=True))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
+    need = ta.attn_bwd_workspace_bytes(1, 3, 777, d)
+    clean = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    stale = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN floats
+    ref = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=causal, workspace=clean)
+    got = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=causal, workspace=stale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        assert torch.equal(a, b), f"{name}: max diff {(a.float() - b.float()).abs().max().item():.3e}"
+    assert not torch.isnan(stale.view(torch.float32)).any()  # every row term was written
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_bwd_ex_empty_sides(d):
     q = torch.randn(1, 2, 70, d, device="cuda").to(torch.bfloat16)
     kv = torch.randn(1, 2, 90, d, device="cuda").to(torch.bfloat16)
