@@ -5,7 +5,9 @@ reads the fixed scratch array the first call left filled), each against
 attn_bwd_ex on the same inputs with a workspace of its own: the two run the
 same kernels on the same row terms, so the gradients must agree bit for bit,
 which is inside the bf16 bar (max abs error <= 2e-2) the parity tests hold
-attn_bwd_ex to against the float64 oracle.
+attn_bwd_ex to against the float64 oracle. Then the same entry point under HIP
+graph capture (beside a key-split forward given its workspace), replayed three
+times against the eager results.
 """
 
 import pytest
@@ -42,3 +44,38 @@ def test_noalloc_backward_two_calls_second_smaller():
     small = Workload("noalloc_b1h2_nq200_nk150_d64", 1, 2, 200, 64, "bf16", seed=72, n_k=150, q_std=3.0)
     _run(big, causal=True)
     _run(small, causal=False)
+
+
+def test_noalloc_backward_under_graph_capture():
+    # The callers this entry point is for include code under HIP graph capture:
+    # a graph holding a key-split forward (workspace given) and the
+    # allocation-free backward replays to the eager results, bit for bit, three
+    # times, with eager work and synchronisations between the replays.
+    w = Workload("noalloc_graph_b1h2_nq300_nk260_d128_causal", 1, 2, 300, 128, "bf16", seed=73, n_k=260)
+    x = {k: t.cuda() for k, t in make_inputs(w, with_grad_output=True).items()}
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o_ref, lse_ref = ta.attn_fwd_ex(q, k, v, w.scale, causal=True, num_splits=2)
+    g_ref = ta.attn_bwd_ex(q, k, v, o_ref, do, lse_ref, w.scale, causal=True)
+    ws = torch.empty(ta.attn_fwd_ex_workspace_bytes(1, 2, 300, 260, 128, 2), dtype=torch.uint8, device="cuda")
+    o, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
+    grads = [torch.empty_like(t) for t in g_ref]
+
+    def step():
+        ta.attn_fwd_ex(q, k, v, w.scale, causal=True, num_splits=2, out=o, lse=lse, workspace=ws)
+        ta.attn_bwd_ex_noalloc(q, k, v, o, do, lse, w.scale, causal=True, dq=grads[0], dk=grads[1], dv=grads[2])
+
+    step()  # eager once first (the library looks up its per-device state here, not under capture)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for t in [o, lse] + grads:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+        for name, a, b in zip(("dQ", "dK", "dV"), grads, g_ref):
+            assert torch.equal(a, b), f"{name}: max diff {(a.float() - b.float()).abs().max().item():.3e}"
+
