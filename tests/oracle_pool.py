@@ -54,11 +54,32 @@ def forward_all(q, k, v, scale, causal=False, row_block=None):
     return o, lse
 
 
-def backward_all(q, k, v, do, scale, causal=False):
-    """Oracle dQ, dK, dV for every head of float64 [B, H, N, d] inputs."""
+def backward_given_o(q, k, v, o, do, scale, causal=False):
+    """Oracle dQ, dK, dV of one head when the row terms D_i = dO_i . O_i are
+    taken from the given O, the output the backward is handed (the forward's
+    stored, rounded result), instead of the exact one.
+
+    The pages print no backward; the reading here (as in the kernel) takes D
+    from the O passed in. dS = P * (dP - D) is linear in D, so with
+    delta_i = dO_i . (O_i - O_exact_i) the exact gradients move by
+    dQ: -scale * delta_i * (P K)_i and dK: -scale * P^T (delta * Q), dV not at
+    all. Both terms are oracle evaluations: P K is the attention output with K
+    in place of V, and P^T Y is dV for the output gradient Y. When the given O
+    is the exact one, delta = 0 and this is attention_backward itself.
+    """
+    dq, dk, dv = attention_backward(q, k, v, do, scale, causal=causal)
+    o_exact, _ = attention_forward(q, k, v, scale, causal=causal)
+    delta = np.sum(do * (o - o_exact), axis=-1, keepdims=True)
+    pk, _ = attention_forward(q, k, k, scale, causal=causal)
+    _, _, pty = attention_backward(q, k, v, delta * q, scale, causal=causal)
+    return dq - scale * delta * pk, dk - scale * pty, dv
+
+
+def backward_all(q, k, v, o, do, scale, causal=False):
+    """backward_given_o for every head of float64 [B, H, N, d] inputs."""
     B, H = q.shape[:2]
     heads = [(b, h) for b in range(B) for h in range(H)]
-    out = _run([lambda bh=bh: attention_backward(q[bh], k[bh], v[bh], do[bh], scale, causal=causal)
+    out = _run([lambda bh=bh: backward_given_o(q[bh], k[bh], v[bh], o[bh], do[bh], scale, causal=causal)
                 for bh in heads])
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     for bh, (gq, gk, gv) in zip(heads, out):

@@ -46,7 +46,8 @@ BF16_U = 2.0 ** -8  # unit roundoff of bf16 round-to-nearest-even (8 significant
 
 
 def _assert_grad(name, got, want):
-    """A gradient within 2e-2 + 2u max|ref| (one u for the rounding of the
+    """A gradient (against the oracle at the given O, oracle_pool's
+    backward_given_o) within 2e-2 + 2u max|ref| (one u for the rounding of the
     result to bf16, one for the bf16 rounding of the P and dS operands), and
     within 2e-2 max|ref| + 1e-4 (a wrongly scaled result fails). Needed where
     gradients grow past ~2: under the mask with N_q > N_k the first visible
@@ -393,13 +394,14 @@ def test_workload_decode_every_head():
 # backward with the mask and unequal lengths
 # ---------------------------------------------------------------------------
 
-def _check_bwd(x, dq, dk, dv, scale, causal, heads=None):
-    from oracle import attention_backward
+def _check_bwd(x, o, dq, dk, dv, scale, causal, heads=None):
+    from oracle_pool import backward_given_o
     q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    o = to_f64(o)
     g = [to_f64(t) for t in (dq, dk, dv)]
     heads = heads if heads is not None else list(np.ndindex(*q.shape[:2]))
     for (b, h) in heads:
-        ref = attention_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal=causal)
+        ref = backward_given_o(q[b, h], k[b, h], v[b, h], o[b, h], do[b, h], scale, causal=causal)
         for name, got, want in zip(("dQ", "dK", "dV"), g, ref):
             _assert_o(f"{name}[{b},{h}]", got[b, h], want, BF16_TOL, BF16_REL)
 
@@ -414,7 +416,7 @@ def test_bwd_ex_small(Nq, Nk, d, causal):
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
     dq, dk, dv = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=causal)
     torch.cuda.synchronize()
-    _check_bwd(x, dq, dk, dv, w.scale, causal)
+    _check_bwd(x, o, dq, dk, dv, w.scale, causal)
     if causal and Nq > Nk:  # queries that see no key get dQ = 0 exactly
         assert torch.all(dq[:, :, :Nq - Nk] == 0)
 
@@ -468,7 +470,7 @@ def test_workload_causal_fwd_bwd_every_head():
     torch.cuda.synchronize()
     _check_whole(x, o, lse, w.scale, True)
     q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
-    ref = backward_all(q, k, v, do, w.scale, causal=True)
+    ref = backward_all(q, k, v, to_f64(o), do, w.scale, causal=True)
     for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         got = to_f64(got)
         for (b, h) in np.ndindex(w.B, w.H):
@@ -491,7 +493,7 @@ def test_long_sequence_fwd_bwd_whole(causal):
     dq, dk, dv = ta.attn_bwd_ex(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale, causal=causal)
     torch.cuda.synchronize()
     _check_whole(x, o, lse, w.scale, causal)
-    _check_bwd(x, dq, dk, dv, w.scale, causal)
+    _check_bwd(x, o, dq, dk, dv, w.scale, causal)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -507,7 +509,7 @@ def test_many_heads_fwd_bwd_whole(d, causal):
     torch.cuda.synchronize()
     _check_whole(x, o, lse, w.scale, causal)
     q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
-    ref = backward_all(q, k, v, do, w.scale, causal=causal)
+    ref = backward_all(q, k, v, to_f64(o), do, w.scale, causal=causal)
     for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         got = to_f64(got)
         for (b, h) in np.ndindex(w.B, w.H):

@@ -19,6 +19,13 @@ result alone is up to u 16 = 0.06, more than 2e-2. The relative check
 floor is for results that vanish analytically, such as dK with a single key,
 which come back at rounding level). fp32 O: <= 1e-5. LSE <= 1e-3 absolute.
 Rows that see no key come back as exactly O = 0, LSE = -inf, dQ = 0.
+
+Gradient reference: the oracle gradient with the row terms D_i = dO_i . O_i
+taken from the O the backward is handed (oracle_pool.backward_given_o), as
+the kernel takes them. The exact gradient differs from it by a term from the
+bf16 rounding of O, which exceeds the relative check where cancellation
+leaves a gradient small (one query against a peaked softmax: |dQ| ~ 7e-3 with
+a 2.5e-3 shift).
 """
 
 import random
@@ -29,7 +36,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import tiled_attention_17_amd as ta  # noqa: E402
-from oracle import attention_backward, attention_forward  # noqa: E402
+from oracle import attention_forward  # noqa: E402
+from oracle_pool import backward_given_o  # noqa: E402
 from tiled_attention_17_amd.workloads import Workload, make_inputs, to_f64  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -115,7 +123,7 @@ def test_random_configuration(case):
             err = float(np.max(np.abs(gl[b, h][~empty] - rl[~empty])))
             assert err <= LSE_TOL, f"LSE[{b},{h}]: max abs err {err:.3e} > {LSE_TOL:.1e}"
         if c["bwd"]:
-            ref = attention_backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, causal=c["causal"])
+            ref = backward_given_o(q[b, h], k[b, h], v[b, h], go[b, h], do[b, h], w.scale, causal=c["causal"])
             for name, got, want in zip(("dQ", "dK", "dV"), grads, ref):
                 _assert_close(f"{name}[{b},{h}]", got[b, h], want, BF16_TOL, BF16_REL, grad=True)
             assert np.all(grads[0][b, h][empty] == 0), f"dQ[{b},{h}]: rows without keys are not 0"
