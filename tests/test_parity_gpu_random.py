@@ -65,7 +65,7 @@ def _draw_cases(n, seed):
     return cases
 
 
-CASES = _draw_cases(28, seed=20261203)
+CASES = _draw_cases(96, seed=20261203)
 
 
 @pytest.fixture(scope="module", autouse=True)
