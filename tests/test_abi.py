@@ -273,3 +273,25 @@ def test_bwd_noalloc_rejects_before_any_gpu_call():
     p2[6] = p2[0] + 64  # dq inside q
     assert lib.attn_bwd_ex_noalloc(*p2, 1, 2, 128, 256, 64, 0.125, 0, 0, None) == 1 and "overlaps" in _err()
     assert lib.attn_bwd_ex_noalloc(*([0] * 9), 1, 2, 0, 0, 64, 0.125, 0, 0, None) == 0
+
+
+def test_header_and_library_from_plain_c(tmp_path):
+    # The boundary is a C ABI: tests/c/abi_from_c.c includes the header with a C
+    # compiler in strict C99, links against the shared library and makes the
+    # calls that need no GPU (version, status strings, workspace sizes, argument
+    # rejection before any HIP call).
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.dirname(ta.LIB_PATH)
+    exe = tmp_path / "abi_from_c"
+    src = os.path.join(os.path.dirname(__file__), "c", "abi_from_c.c")
+    inc = os.path.join(os.path.dirname(__file__), os.pardir, "include")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", inc, src, "-o", str(exe),
+                    "-L", lib_dir, "-ltiledattn", f"-Wl,-rpath,{lib_dir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 9, r.stdout
