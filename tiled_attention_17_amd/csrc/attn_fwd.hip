@@ -14,9 +14,12 @@
 //     statistics m and l, the rescale factor alpha and 1/l are per-lane
 //     scalars and need one cross-half exchange (v_permlane32_swap) per tile;
 //   * Q^T (the B operand) stays in VGPRs for the whole key sweep;
-//   * K and V tiles (64 keys) are staged through LDS, double-buffered, with
-//     16-byte coalesced global loads; K rows are placed at swap23(key) so the
-//     score accumulator is already in the operand order of the next product;
+//   * K and V tiles (128 keys in the 256-query ping-pong kernel, 64 in the
+//     smaller kernels) are staged through LDS, double-buffered: K goes
+//     straight from memory to LDS (buffer_load ... lds, 16 bytes per lane),
+//     V through registers (16-byte loads); K rows are placed at swap23(key)
+//     so the score accumulator is already in the operand order of the next
+//     product;
 //   * V is stored TRANSPOSED in LDS (V^T, one row of 64 keys per d), so the
 //     A operand of O^T += V^T P^T is one ds_read_b128 per MFMA. The
 //     transpose is done once per workgroup while staging: each lane loads the
