@@ -1,11 +1,11 @@
-"""Profiling driver for the forward kernel and the summary of its counter runs.
+"""Profiling runs of the attention kernels and the summaries of their counter runs.
 
   python -m tiled_attention_17_amd.profiling run [--launches 5] [--copy-mib 1024]
       Enqueues one plain device-to-device copy of a known size (the
       calibration kernel for HBM byte counters) and then `launches` forward
       passes of the headline workload (B=2, H=16, N=4096, d=128, bf16).
       Meant to run under rocprofv3, e.g.
-        rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv \
+        rocprofv3 --pmc FETCH_SIZE -d OUT/pmc_fetch -o run --output-format csv \
             -- python -m tiled_attention_17_amd.profiling run
 
   python -m tiled_attention_17_amd.profiling run-set [--launches 3] [--copy-mib 1024]
@@ -200,17 +200,17 @@ def summarize_set(sq_dir, fetch_dir, write_dir, copy_mib, out_md):
     gs, gf, gw = groups(sq), groups(fe), groups(wr)
     mean = lambda ds, k: sum(d.get(k, 0.0) for d in ds) / len(ds)
     lines = ["# Hardware counters per kernel (one MI355X)", "",
-             "Three rocprofv3 runs of the same program (repo root on the box), each with counters the",
+             "Three rocprofv3 runs of the same program (repo root, on the MI355X), each with counters the",
              "hardware collects in one pass:", "",
              "    rocprofv3 --pmc " + " ".join(SET_SQ_COUNTERS) + " \\",
-             "        -d gpurun_out/pmc_set_sq -o run --output-format csv \\",
+             f"        -d {sq_dir} -o run --output-format csv \\",
              "        -- python3 tiled_attention_17_amd/profiling.py run-set",
-             "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_set_fetch -o run --output-format csv \\",
+             f"    rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv \\",
              "        -- python3 tiled_attention_17_amd/profiling.py run-set",
-             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_set_write -o run --output-format csv \\",
+             f"    rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run --output-format csv \\",
              "        -- python3 tiled_attention_17_amd/profiling.py run-set",
-             "    python3 -m tiled_attention_17_amd.profiling summarize-set --sq gpurun_out/pmc_set_sq \\",
-             "        --fetch gpurun_out/pmc_set_fetch --write gpurun_out/pmc_set_write", "",
+             f"    python3 -m tiled_attention_17_amd.profiling summarize-set --sq {sq_dir} \\",
+             f"        --fetch {fetch_dir} --write {write_dir}", "",
              "Columns (means over a kernel's dispatches in the SQ run; counter runs serialize the",
              "dispatches, so the clock here is not the one of a sustained run, and for kernels of a few",
              "tens of microseconds the GRBM window also spans the dispatch itself, which inflates the",
@@ -314,12 +314,12 @@ def summarize(fetch_dir, write_dir, stats_dir, copy_mib, out_json, out_txt):
     lines = [f"# HBM traffic of {FWD_KERNEL} on {w.name}", "",
              "Counters FETCH_SIZE and WRITE_SIZE (one rocprofv3 --pmc run each), scaled by the",
              f"same counters on a {copy_mib} MiB device-to-device copy. Commands (repo root):", "",
-             "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv \\",
+             f"    rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv \\",
              "        -- python3 tiled_attention_17_amd/profiling.py run",
-             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv \\",
+             f"    rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run --output-format csv \\",
              "        -- python3 tiled_attention_17_amd/profiling.py run",
-             "    python3 -m tiled_attention_17_amd.profiling summarize --fetch gpurun_out/pmc_fetch \\",
-             "        --write gpurun_out/pmc_write", "",
+             f"    python3 -m tiled_attention_17_amd.profiling summarize --fetch {fetch_dir} \\",
+             f"        --write {write_dir}", "",
              f"The copy reads {copy_bytes} bytes and writes as many; the counters read "
              f"{max(fc):.0f} and {max(wc):.0f} units for it, which gives the scale factors below.", ""]
     for k, v in res.items():
@@ -370,7 +370,7 @@ def summarize_bench(trace_dir, bench_line, cmd, out_md):
         g[3] = max(g[3], ns)
     lines = [
         f"# Kernel trace of the benchmark command: headline forward {line['config']['workload']}", "",
-        "Command (repo root on the MI355X box):", "",
+        "Command (repo root, on the MI355X):", "",
         f"    {cmd}", "",
         "## Headline forward: the timed launches", "",
         f"bench.py launched the headline forward {ex['settle_launches']} times to settle the clock "
@@ -482,7 +482,7 @@ def mfma_ceiling(iters, settle_ms, out_md, command):
         "The LDS modes keep two operand reads in flight per wave, so part of their drop is read latency;",
         "their clocks show what the reads add to the power.",
         "",
-        "Command (repo root on the box):",
+        "Command (repo root, on the MI355X):",
         "",
         f"    {command}",
         "",
