@@ -19,9 +19,11 @@ launch stream, repeat, verify the outputs):
   * every timed launch is bracketed by its own start and end events, so the
     per-launch kernel time (mean, median, min) is reported beside the
     whole-region step time;
-  * the short configurations (fp32 single head, d = 64) are also timed cold:
-    a 1 GiB scratch write between launches evicts the L2s and the Infinity
-    Cache, and each launch is timed on its own;
+  * the short configurations (fp32 single head, d = 64) are also timed cold
+    (a 1 GiB scratch write between launches evicts the L2s and the Infinity
+    Cache, and each launch is timed on its own) and back to back (a burst of
+    launches between one pair of events, without the per-launch events whose
+    own overhead is a sizeable part of a launch of a few microseconds);
   * the outputs of the timed launches are kept and compared with the oracle
     in the CPU leg (whole heads of the headline workload, every head of the
     d = 64 and fp32 workloads, sampled rows of the long sequence, sampled
@@ -116,6 +118,24 @@ def time_launches(fn, stream, n, warm, settle_ms):
             "settle_ms": spent, "settle_launches": settle_launches}
 
 
+def time_burst(fn, stream, n):
+    """Time per launch of n back-to-back launches between one pair of events.
+
+    For kernels of a few microseconds the per-launch events of time_launches
+    add their own overhead to each launch; a burst without them shows what a
+    stream of such launches costs (the dispatch gaps between them included).
+    """
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return {"ms_per_launch": a.elapsed_time(b) / n, "launches": n}
+
+
 def time_cold(fn, stream, n, scratch):
     """Per-launch time with the caches evicted before each launch (1 GiB scratch write)."""
     import torch
@@ -200,6 +220,8 @@ def measure_configs(ta, pm, dev, stream, n, settle_ms, checks):
         r = {"workload": w.name, "cache": "warm (inputs resident in L2 / Infinity Cache across launches)",
              **t, **_rates(pm, fl, nb, t["kernel_ms_mean"], dt), "algorithmic_bytes": nb}
         if not long:
+            bb = time_burst(fwd, stream, 10 * n)
+            r["back_to_back"] = {**bb, **_rates(pm, fl, nb, bb["ms_per_launch"], dt)}
             c = time_cold(fwd, stream, n, scratch)
             r["cold"] = {**c, **_rates(pm, fl, nb, c["kernel_ms_median"], dt)}
         out[key] = r
