@@ -295,3 +295,36 @@ def test_header_and_library_from_plain_c(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 9, r.stdout
+
+
+def test_last_error_is_per_thread():
+    # attn_last_error is thread-local: two threads making different bad calls
+    # at the same time each read back their own message (ctypes releases the
+    # interpreter lock around the foreign calls, so the calls interleave).
+    import threading
+
+    lib = ctypes.CDLL(ta.LIB_PATH)
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                                           ctypes.c_void_p]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    bad = []
+
+    def worker(kw, needle):
+        args = dict(q=A, k=A + T, v=A + 2 * T, o=A + 3 * T, lse=A + 4 * T, B=1, H=2, N=128, d=64)
+        args.update(kw)
+        for _ in range(3000):
+            lib.attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"],
+                         args["N"], args["d"], 0.125, 0, None)
+            if needle not in lib.attn_last_error().decode():
+                bad.append(needle)
+                return
+
+    ts = [threading.Thread(target=worker, args=(dict(q=0), "q is NULL")),
+          threading.Thread(target=worker, args=(dict(d=96), "d=96")),
+          threading.Thread(target=worker, args=(dict(B=-1), "negative size"))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad, bad
