@@ -121,18 +121,21 @@ def test_causal_fp32(N, d):
     _check(x, o, lse, w.scale, True, FP32_TOL, None)
 
 
-@pytest.mark.parametrize("ksplit", ["1", "2"])
+@pytest.mark.parametrize("ksplit", ["1", "2", "2/32"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Nq,Nk", [(1, 1), (37, 37), (64, 64), (100, 100), (257, 257), (777, 777),
                                    (150, 90), (40, 1000)])
 def test_fp32_keys_split_in_workgroup(Nq, Nk, d, causal, ksplit, monkeypatch):
     # fp32 forward with a workgroup's key tiles dealt out to its waves and
-    # merged through LDS (2) and with one key loop per wave (1): fewer tiles
-    # than waves (waves without a key), tile counts not a multiple of the
-    # waves, a ragged last tile, N_q != N_k (rows without a visible key under
-    # the mask) and a large query spread.
-    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", ksplit)
+    # merged through LDS (2; at d = 64 and these grid sizes the 16-query
+    # 16x16x4 kernel, and "2/32" the 32-query one) and with one key loop per
+    # wave (1): fewer tiles than waves (waves without a key), tile counts not
+    # a multiple of the waves, a ragged last tile, N_q != N_k (rows without a
+    # visible key under the mask) and a large query spread.
+    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", ksplit.split("/")[0])
+    if ksplit == "2/32":
+        monkeypatch.setenv("TILED_ATTN_FWD_F32_BM", "32")
     w = _wl(1, 2, Nq, Nk, d, dtype="fp32", seed=600 + Nq + Nk + d, q_std=3.0, causal=causal)
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)
@@ -140,10 +143,11 @@ def test_fp32_keys_split_in_workgroup(Nq, Nk, d, causal, ksplit, monkeypatch):
     _check(x, o, lse, w.scale, causal, FP32_TOL, None)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("ksplit", ["1", "2"])
-def test_fp32_keys_split_in_workgroup_with_key_splits(ksplit, monkeypatch):
+def test_fp32_keys_split_in_workgroup_with_key_splits(ksplit, d, monkeypatch):
     monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", ksplit)
-    w = _wl(2, 1, 70, 1500, 128, dtype="fp32", seed=610)
+    w = _wl(2, 1, 70, 1500, d, dtype="fp32", seed=610)
     x = _cuda(make_inputs(w))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=True, num_splits=3)
     torch.cuda.synchronize()

@@ -134,6 +134,15 @@ int env_ksplit() {
   return (k == 1 || k == 2) ? k : 0;
 }
 
+// TILED_ATTN_FWD_F32_BM=16 or 32 fixes the query tile of the fp32 key-split
+// kernel at d = 64 (16: the 16x16x4 MFMA kernel for the smallest grids).
+int env_f32_bm() {
+  const char* s = std::getenv("TILED_ATTN_FWD_F32_BM");
+  if (!s) return 0;
+  const int b = std::atoi(s);
+  return (b == 16 || b == 32) ? b : 0;
+}
+
 // TILED_ATTN_FWD_DECODE=1 keeps bf16 launches with one query per head on
 // the tiled kernels instead of the one-query kernel.
 int env_decode() {
@@ -222,7 +231,7 @@ attn_status fwd_common(const void* q, const void* k, const void* v, void* o, flo
   if (cus == 0 && (s = device_cus(&cus)) != ATTN_OK) return s;
   tattn::FwdArgs a{q, k, v, o, lse, bh, Nq, Nk, d, scale, dtype == ATTN_FP32,
                    mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves(),
-                   env_ksplit(), env_decode()};
+                   env_ksplit(), env_decode(), env_f32_bm()};
   const hipError_t he = tattn::launch_attn_fwd(a);
   if (he != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(he));
   return ok();

@@ -1231,6 +1231,206 @@ __global__ __launch_bounds__(FwdF32SplitCfg<D>::NG * 64) void attn_fwd_f32_kspli
   }
 }
 
+// fp32 key split for the smallest grids (d = 64): 16 queries per workgroup
+// on v_mfma_f32_16x16x4_f32, so that a grid of few 32-query tiles (one head
+// of 256 queries: 8 workgroups) spreads over twice the compute units; the
+// fp32 matrix rate per SIMD is the same for both shapes. Four waves (key
+// groups) per workgroup, one per SIMD, K and V straight from memory into
+// registers, as in the 32-query kernel above. Lane l = 16 g + c holds query
+// c of the tile; its accumulator slot 4 kb + i holds key 16 kb + 4 g + i of a
+// 32-key tile, and the four lanes of a query (g = 0..3) hold its keys in
+// turn, so the row maximum and sum take two cross-lane steps.
+template <int D>
+struct FwdF32Split16Cfg {
+  static constexpr int NG = 4;         // waves (key groups) per workgroup
+  static constexpr int BM = 16;        // queries per workgroup
+  static constexpr int BN = 32;        // keys per tile: two 16-key blocks
+  static constexpr int DQ = D / 4;     // d-values per lane group of the score operands
+  static constexpr int DB = D / 16;    // 16-row blocks of O^T
+  static constexpr int NV = 8 * DB;    // V operand values per lane and tile
+  static constexpr int NE = 4 * DB + 2;  // floats one lane hands over: o, m, l
+};
+
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(FwdF32Split16Cfg<D>::NG * 64) void attn_fwd_f32_ksplit16_kernel(
+    const FwdParams p) {
+  using C = FwdF32Split16Cfg<D>;
+  __shared__ float xch[(C::NG - 1) * C::NE * 64];
+
+  const TileId ti = decode_tile(p);
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q_row = ti.qt * C::BM + lc;
+  const bool q_ok = q_row < p.Nq;
+  const KeyRange kr = key_range<C::BN>(p, ti.split, ti.qt * C::BM, C::BM);
+  const int kmax = row_kmax(p, kr, q_row);
+  const float* Kh = (const float*)p.k + (size_t)ti.bh * p.Nk * D;
+  const float* Vh = (const float*)p.v + (size_t)ti.bh * p.Nk * D;
+
+  // Score operands: step s of lane group lg contracts d = lg D/4 + s (any
+  // assignment of d to the steps gives the same dot product; this one keeps
+  // a lane's share of a Q or K row contiguous).
+  float qf[C::DQ];
+  {
+    const __amdgpu_buffer_rsrc_t qr = f32_rows_rsrc<D>((const float*)p.q + (size_t)ti.bh * p.Nq * D,
+                                                       ti.qt * C::BM, C::BM, p.Nq);
+#pragma unroll
+    for (int c = 0; c < C::DQ / 4; ++c) {
+      const f32x4 x = buffer_load_f32x4(qr, 4 * (lc * D + lg * C::DQ + 4 * c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * c + e] = x[e];
+    }
+  }
+
+  // Tile j: K rows as the A operand of S^T = K Q^T (block kb: lane holds key
+  // 16 kb + lc, its d-quarter lg); V as the A operand of O^T += V^T P^T
+  // (lane: d = 16 db + lc; step 4 kb + i takes key 16 kb + 4 lg + i, the key
+  // of accumulator slot 4 kb + i). Rows past N_k read as zero.
+  auto load_tile = [&](int j, float* kd, float* vd) {
+    const int key0 = kr.k_begin + j * C::BN;
+    const __amdgpu_buffer_rsrc_t kr_ = f32_rows_rsrc<D>(Kh, key0, C::BN, p.Nk);
+    const __amdgpu_buffer_rsrc_t vr_ = f32_rows_rsrc<D>(Vh, key0, C::BN, p.Nk);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < C::DQ / 4; ++c) {
+        const f32x4 x = buffer_load_f32x4(kr_, 4 * ((16 * kb + lc) * D + lg * C::DQ + 4 * c));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kd[kb * C::DQ + 4 * c + e] = x[e];
+      }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        vd[t * C::DB + db] =
+            buffer_load_f32(vr_, 4 * ((16 * (t >> 2) + 4 * lg + (t & 3)) * D + 16 * db + lc));
+  };
+
+  f32x4 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int n_mine = kr.n_tiles > g ? (kr.n_tiles - g + C::NG - 1) / C::NG : 0;
+  float kn[2 * C::DQ], vn[C::NV];
+  if (n_mine > 0) load_tile(g, kn, vn);
+  for (int i = 0; i < n_mine; ++i) {
+    const int j = g + C::NG * i;
+    const int key0 = kr.k_begin + j * C::BN;
+    float kc[2 * C::DQ], vc[C::NV];
+#pragma unroll
+    for (int e = 0; e < 2 * C::DQ; ++e) kc[e] = kn[e];
+#pragma unroll
+    for (int e = 0; e < C::NV; ++e) vc[e] = vn[e];
+    // Unconditional (the last step reloads its own tile): a load under a
+    // branch would make the compiler wait for it where the paths join.
+    load_tile(i + 1 < n_mine ? j + C::NG : j, kn, vn);
+
+    // S^T of the two 16-key blocks: two independent chains over d.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::DQ; ++s) {
+      s0 = mfma16x16x4f32(kc[s], qf[s], s0);
+      s1 = mfma16x16x4f32(kc[C::DQ + s], qf[s], s1);
+    }
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = s0[e];
+      sv[4 + e] = s1[e];
+    }
+
+    // key of slot e: key0 + 16 (e/4) + 4 lg + e%4; keys past kmax are dropped
+    const bool masked = j >= kr.n_full;
+    if (masked) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key0 + 16 * (e >> 2) + 4 * lg + (e & 3) > kmax) sv[e] = -INFINITY;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = max_with_other_half(mx);
+    // A row with no visible key so far keeps m = -inf, l = 0, o = 0.
+    const float mt = mx == -INFINITY ? -INFINITY : mx * p.c;
+    const float m_new = fmaxf(m_run, mt);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    float pr[8], lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pr[e] = fast_exp2(fmaf(sv[e], p.c, -m_ref));
+      if (masked && sv[e] == -INFINITY) pr[e] = 0.f;
+      lsum += pr[e];
+    }
+    l_run = fmaf(alpha, l_run, lsum);
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] = mfma16x16x4f32(vc[t * C::DB + db], pr[t], oacc[db]);
+  }
+
+  // Hand-over ([wave - 1][element][lane]) and merge in wave 0:
+  // m = max_g m_g, l = sum_g 2^(m_g - m) l_g, o likewise.
+  float* xb = xch + lane;
+  if (g > 0) {
+    float* w = xb + (size_t)(g - 1) * C::NE * 64;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[(4 * db + e) * 64] = oacc[db][e];
+    w[(C::NE - 2) * 64] = m_run;
+    w[(C::NE - 1) * 64] = l_run;
+  }
+  __syncthreads();
+  if (g > 0) return;
+  float m = m_run;
+  for (int k = 0; k < C::NG - 1; ++k) m = fmaxf(m, xb[(k * C::NE + C::NE - 2) * 64]);
+  const float m_ref = m == -INFINITY ? 0.f : m;  // no group saw a visible key
+  const float a0 = fast_exp2(m_run - m_ref);
+  float l = a0 * l_run;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) oacc[db][e] *= a0;
+  for (int k = 0; k < C::NG - 1; ++k) {
+    const float* r = xb + (size_t)k * C::NE * 64;
+    const float a = fast_exp2(r[(C::NE - 2) * 64] - m_ref);
+    l = fmaf(a, r[(C::NE - 1) * 64], l);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[db][e] = fmaf(a, r[(4 * db + e) * 64], oacc[db][e]);
+  }
+
+  // each lane summed its own keys: add the query's four lanes
+  float l_tot = l + __shfl_xor(l, 16, 64);
+  l_tot = add_other_half(l_tot);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_ok) {
+    const bool part = p.n_splits > 1;
+    const size_t row = part ? ((size_t)ti.split * p.BH + ti.bh) * p.Nq + q_row
+                            : (size_t)ti.bh * p.Nq + q_row;
+    float* orow = (part ? p.o_part : (float*)p.o) + row * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const f32x4 w = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+      *(f32x4*)(orow + 16 * db + 4 * lg) = w;
+    }
+    if (lg == 0) (part ? p.lse_part : p.lse)[row] = (m + fast_log2(l_tot)) * kLn2;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // merge of key-split partial results
 // ---------------------------------------------------------------------------
@@ -1354,7 +1554,14 @@ static bool use_ksplit(const FwdArgs& a, int64_t splits, int nw) {
 }
 
 template <int D>
-static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total, bool ksplit) {
+static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total, bool ksplit, bool small) {
+  if constexpr (D == 64) {
+    if (small) {
+      hipLaunchKernelGGL((attn_fwd_f32_ksplit16_kernel<D>), dim3((unsigned)total),
+                         dim3(FwdF32Split16Cfg<D>::NG * 64), 0, (hipStream_t)a.stream, p);
+      return hipGetLastError();
+    }
+  }
   if (ksplit)
     hipLaunchKernelGGL((attn_fwd_f32_ksplit_kernel<D>), dim3((unsigned)total),
                        dim3(FwdF32SplitCfg<D>::NG * 64), 0, (hipStream_t)a.stream, p);
@@ -1372,6 +1579,16 @@ static bool use_f32_ksplit(const FwdArgs& a) {
   const int64_t tiles = a.BH * ((a.Nq + FwdF32Cfg<64>::BM - 1) / FwdF32Cfg<64>::BM) *
                         (a.n_splits > 1 ? a.n_splits : 1);
   return tiles < (int64_t)a.num_cus;
+}
+
+// fp32 at d = 64: 16-query tiles (the 16x16x4 kernel) when even the key
+// split's 32-query tiles would leave more than half of the compute units idle.
+static bool use_f32_small(const FwdArgs& a, bool ksplit) {
+  if (a.d != 64 || !ksplit || a.f32_bm == 32) return false;
+  if (a.f32_bm == 16) return true;
+  const int64_t tiles = a.BH * ((a.Nq + FwdF32SplitCfg<64>::BM - 1) / FwdF32SplitCfg<64>::BM) *
+                        (a.n_splits > 1 ? a.n_splits : 1);
+  return 2 * tiles <= (int64_t)a.num_cus;
 }
 
 // Workgroup size choice: the largest query tile whose grid (with the key
@@ -1422,10 +1639,11 @@ int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) 
 hipError_t launch_attn_fwd(const FwdArgs& a) {
   int64_t total = 0;
   if (a.dtype_fp32) {
-    const bool ks = use_f32_ksplit(a);
-    const FwdParams p = make_params(a, ks ? FwdF32SplitCfg<64>::BM : FwdF32Cfg<64>::BM, &total);
+    const bool ks = use_f32_ksplit(a), small = use_f32_small(a, ks);
+    const FwdParams p = make_params(a, small ? FwdF32Split16Cfg<64>::BM : ks ? FwdF32SplitCfg<64>::BM
+                                                                          : FwdF32Cfg<64>::BM, &total);
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipError_t e = a.d == 64 ? launch_f32<64>(a, p, total, ks) : launch_f32<128>(a, p, total, ks);
+    hipError_t e = a.d == 64 ? launch_f32<64>(a, p, total, ks, small) : launch_f32<128>(a, p, total, ks, false);
     if (e != hipSuccess || p.n_splits == 1) return e;
     return launch_attn_merge(p.o_part, p.lse_part, p.n_splits, a.BH * a.Nq, a.d, a.o, a.lse, true,
                              a.stream);

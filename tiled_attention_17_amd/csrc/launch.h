@@ -28,6 +28,7 @@ struct FwdArgs {
                     // where the launch allows it (bf16: two wave groups, no mask, no key splits,
                     // waves < 8; fp32: always)
   int decode;       // 0 = choose; 1 = never use the one-query kernel for N_q = 1 (bf16)
+  int f32_bm;       // 0 = choose; 16 or 32 = query tile of the fp32 key-split kernel (d = 64)
 };
 
 // Parameters of one forward kernel launch (kernel argument, by value).
