@@ -16,9 +16,13 @@ launch stream, repeat, verify the outputs):
     over tens of milliseconds, so before the timed region each measurement
     launches its kernel until --settle-ms of GPU time have passed (whatever
     --warmup says), then --warmup more launches;
-  * every timed launch is bracketed by its own start and end events, so the
-    per-launch kernel time (mean, median, min) is reported beside the
-    whole-region step time;
+  * every timed launch has its own start and end events, so the per-launch
+    kernel time (mean, median, min) is reported beside the whole-region step
+    time; for the forward launches of the headline and of the fp32, d = 64
+    and long-sequence workloads the library binds the two events to the
+    start and end of the attention kernel's dispatch (attn_fwd_ex_timed), so
+    they time the kernel alone and put no event commands between the
+    launches; the other measurements record their events around the call;
   * the short configurations (fp32 single head, d = 64) are also timed cold
     (a 1 GiB scratch write between launches evicts the L2s and the Infinity
     Cache, and each launch is timed on its own) and back to back (a burst of
@@ -77,12 +81,24 @@ def measured_traffic():
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def time_launches(fn, stream, n, warm, settle_ms):
+def time_launches(fn, stream, n, warm, settle_ms, timed_fn=None):
     """Launch fn until settle_ms of GPU time pass, then warm more, then time n launches.
 
-    Each timed launch has its own start and end event on `stream`; returns
-    per-launch mean / median / min, the whole region's time per launch, and
+    Without timed_fn each timed launch is bracketed by its own start and end
+    events on `stream`. Returns per-launch mean / median / min
+    (kernel_ms_*), the whole region's time per launch (ms_per_launch) and
     what the settle did.
+
+    With timed_fn (fn's call made through attn_fwd_ex_timed, given a start and
+    a stop event that the library binds to its attention kernel's dispatch):
+      * the timed region holds the n launches back to back with only their
+        stop events bound, which adds no command between them (a bound start
+        event is a marker command of its own, ≈5 µs per launch):
+        ms_per_launch is the rate of an uninterrupted stream of launches, and
+        interval_ms_* the time from one kernel's end to the next one's
+        (its duration plus the dispatch gap before it);
+      * then n more launches with both events bound give each kernel's own
+        duration (kernel_ms_*), what a kernel trace shows.
     """
     import torch
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -104,18 +120,36 @@ def time_launches(fn, stream, n, warm, settle_ms):
         fn()
     starts, ends = [ev() for _ in range(n)], [ev() for _ in range(n)]
     t0, t1 = ev(), ev()
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(n):
-        starts[i].record(stream)
-        fn()
-        ends[i].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
+    r = {"launches": n, "warmup": warm, "settle_ms": spent, "settle_launches": settle_launches}
+    if timed_fn is None:
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(n):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+    else:
+        stops = [ev() for _ in range(n)]
+        for e in starts + ends + stops:  # torch creates an event's HIP handle on its first record
+            e.record(stream)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(n):
+            timed_fn(None, stops[i])
+        t1.record(stream)
+        for i in range(n):
+            timed_fn(starts[i], ends[i])
+        torch.cuda.synchronize()
+        iv = sorted(stops[i - 1].elapsed_time(stops[i]) for i in range(1, n))
+        if iv:
+            r.update(interval_ms_mean=sum(iv) / len(iv), interval_ms_median=iv[len(iv) // 2],
+                     interval_ms_min=iv[0])
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return {"kernel_ms_mean": sum(per) / n, "kernel_ms_median": per[n // 2], "kernel_ms_min": per[0],
-            "ms_per_launch": t0.elapsed_time(t1) / n, "launches": n, "warmup": warm,
-            "settle_ms": spent, "settle_launches": settle_launches}
+    r.update(kernel_ms_mean=sum(per) / n, kernel_ms_median=per[n // 2], kernel_ms_min=per[0],
+             ms_per_launch=t0.elapsed_time(t1) / n)
+    return r
 
 
 def time_burst(fn, stream, n):
@@ -211,8 +245,11 @@ def measure_configs(ta, pm, dev, stream, n, settle_ms, checks):
         def fwd():
             ta.attn_fwd(x["q"], x["k"], x["v"], w.scale, out=o, lse=lse)
 
+        def fwd_timed(start, stop):
+            ta.attn_fwd_ex_timed(x["q"], x["k"], x["v"], start, stop, w.scale, out=o, lse=lse)
+
         long = w.N > 4096
-        t = time_launches(fwd, stream, max(5, n // 10) if long else n, 3, settle_ms)
+        t = time_launches(fwd, stream, max(5, n // 10) if long else n, 3, settle_ms, fwd_timed)
         dt = "fp32" if w.dtype == "fp32" else "bf16"
         eb = 4 if dt == "fp32" else 2
         fl = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
@@ -451,8 +488,11 @@ def main():
     def step():
         ta.attn_fwd(x["q"], x["k"], x["v"], w.scale, out=o, lse=lse)
 
+    def step_timed(start, stop):
+        ta.attn_fwd_ex_timed(x["q"], x["k"], x["v"], start, stop, w.scale, out=o, lse=lse)
+
     K = args.steps
-    t = time_launches(step, stream, K, args.warmup, args.settle_ms)
+    t = time_launches(step, stream, K, args.warmup, args.settle_ms, step_timed)
     o_timed, lse_timed = o.cpu(), lse.cpu()  # every launch writes the same result
     ms_per_step = t["ms_per_launch"]
     flops = pm.attn_fwd_flops(w.B, w.H, w.N, w.d)
@@ -468,10 +508,16 @@ def main():
         "kernel_ms_mean": t["kernel_ms_mean"],
         "kernel_ms_median": t["kernel_ms_median"],
         "kernel_ms_min": t["kernel_ms_min"],
+        "interval_ms_mean": t.get("interval_ms_mean"),
+        "interval_ms_median": t.get("interval_ms_median"),
         "algorithmic_bytes_per_launch": nbytes,
         "gb_per_s": nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9,
-        "timing": "per-launch start/end HIP events on the launch stream after a clock settle; "
-                  "headline launches before the timed ones: settle_launches + warmup",
+        "timing": "after a clock settle and the warm-up, K launches back to back between two HIP events on "
+                  "the launch stream, each with only its stop event bound to its kernel's end (value, "
+                  "ms_per_step; interval_ms_*: one kernel's end to the next one's), then K launches with "
+                  "start and stop events bound to each kernel's dispatch by the library "
+                  "(attn_fwd_ex_timed: kernel_ms_*, roofline.achieved); headline launches before the "
+                  "timed ones: settle_launches + warmup",
     }
     checks = []
     sub = max(20, K // 4)

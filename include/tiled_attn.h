@@ -157,6 +157,29 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         size_t workspace_bytes, attn_dtype dtype, void* stream);
 
 /*
+ * attn_fwd_ex that also records how long its attention kernel ran, into two
+ * events of the caller: the timing of GPU work with events on its stream
+ * (Lecture 17 page §10.2), here without event commands of their own between
+ * back-to-back launches, which would add their gaps to the measured time.
+ *   start_event, stop_event
+ *             hipEvent_t handles (passed as void*) that the caller created
+ *             with timing enabled, or NULL. The library binds them to the
+ *             start and the end of the call's attention kernel (its launch
+ *             over the query tiles; the merge of key splits, when there is
+ *             one, runs after stop_event), so that hipEventElapsedTime of the
+ *             two gives that kernel's execution time. A NULL event is not
+ *             touched.
+ * A call that launches nothing (B*H*Nq == 0) or fails its checks leaves both
+ * events as they were. Arguments, results and errors otherwise as for
+ * attn_fwd_ex; an invalid event handle makes the launch fail (ATTN_ERR_HIP).
+ */
+attn_status attn_fwd_ex_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                              attn_mask mask, int64_t num_splits, void* workspace,
+                              size_t workspace_bytes, attn_dtype dtype, void* stream,
+                              void* start_event, void* stop_event);
+
+/*
  * Merge of attention results over disjoint key sets into the result over
  * their union (the rescaling of the online update, Lecture 17 page §8.3,
  * applied to partial results written back to memory, CS336 Lecture 5

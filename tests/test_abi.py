@@ -26,7 +26,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"attn_version", "attn_status_string", "attn_last_error", "attn_fwd",
-                          "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
+                          "attn_fwd_ex", "attn_fwd_ex_timed", "attn_fwd_ex_workspace_bytes",
+                          "attn_fwd_ex_auto_splits",
                           "attn_merge", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_ex",
                           "attn_matmul_nt", "attn_quantize_mxfp8", "attn_fwd_mxfp8", "attn_bwd_ex_noalloc"}
     lib = ctypes.CDLL(ta.LIB_PATH)
@@ -36,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = ta.library()
-    assert lib.attn_version() == 2
+    assert lib.attn_version() == 3
     assert lib.attn_status_string(0) == b"ATTN_OK"
     assert lib.attn_status_string(1) == b"ATTN_ERR_INVALID_ARGUMENT"
     assert lib.attn_status_string(2) == b"ATTN_ERR_UNSUPPORTED"
@@ -133,6 +134,27 @@ def test_fwd_ex_rejects(kw, status, needle):
 def test_fwd_ex_empty_is_noop():
     assert _fwd_ex(q=0, k=0, v=0, o=0, lse=0, Nq=0) == 0
     assert _fwd_ex(q=0, k=0, v=0, o=0, lse=0, B=0, splits=8) == 0
+    assert _err() == ""
+
+
+def _fwd_ex_timed(start, stop, q=A, k=A + T, v=A + 2 * T, o=A + 3 * T, lse=A + 4 * T, B=1, H=2, Nq=128,
+                  Nk=256, d=64, scale=0.125, mask=0, splits=1, ws=None, ws_bytes=0, dt=0):
+    return ta.library().attn_fwd_ex_timed(q, k, v, o, lse, B, H, Nq, Nk, d, scale, mask, splits, ws,
+                                          ws_bytes, dt, None, start, stop)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(mask=2), 1, "unknown mask"),
+    (dict(splits=4), 1, "workspace is NULL"),
+    (dict(d=96), 2, "d=96"),
+    (dict(o=A + 2 * T + 4096), 1, "overlaps input v"),
+])
+def test_fwd_ex_timed_checks_like_fwd_ex(kw, status, needle):
+    # The checks run before anything is enqueued, so the (never used) event
+    # handles are not looked at.
+    assert _fwd_ex_timed(A + 9 * T, A + 10 * T, **kw) == status
+    assert needle in _err()
+    assert _fwd_ex_timed(None, None, q=0, k=0, v=0, o=0, lse=0, Nq=0) == 0
     assert _err() == ""
 
 

@@ -10,6 +10,7 @@ build exports.
 """
 
 import ctypes
+import json
 import os
 
 import numpy as np
@@ -65,7 +66,46 @@ def test_cpu_leg_fails_a_planted_gradient_error():
 def test_ordered_debug_library_exports_the_same_entry_points():
     rel = ctypes.CDLL(os.path.join(os.path.dirname(ta.LIB_PATH), "libtiledattn.so"))
     dbg = ctypes.CDLL(os.path.join(os.path.dirname(ta.LIB_PATH), "libtiledattn_ordered.so"))
-    for name in ("attn_fwd", "attn_fwd_ex", "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_ex_noalloc",
+    for name in ("attn_fwd", "attn_fwd_ex", "attn_fwd_ex_timed", "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_ex_noalloc",
                  "attn_fwd_mxfp8", "attn_quantize_mxfp8", "attn_matmul_nt", "attn_version"):
         assert hasattr(rel, name) and hasattr(dbg, name), name
     assert rel.attn_version() == dbg.attn_version()
+
+
+def test_trace_summary_picks_the_timed_launches(tmp_path):
+    # A synthetic kernel trace in bench.py's launch order: settle + warm-up
+    # launches of the headline forward, the timed region's back-to-back
+    # launches (300 us), the launches with kernel-bound events (250 us), then
+    # other kernels and later forward launches of other shapes.
+    from tiled_attention_17_amd import profiling
+    settle, warm, steps = 7, 2, 4
+    fwd = "void tattn::attn_fwd_bf16_pingpong_kernel<128, 128>(tattn::FwdParams)"
+    durs = [400_000] * (settle + warm) + [300_000] * steps + [250_000, 240_000, 260_000, 250_000]
+    rows, t = [], 0
+    for i, ns in enumerate(durs):
+        rows.append((i + 1, fwd, t, t + ns))
+        t += ns + 1000
+    rows += [(len(rows) + 1, "void tattn::attn_bwd_dkdv_kernel<128>(tattn::BwdParams)", t, t + 90_000),
+             (len(rows) + 2, fwd, t + 100_000, t + 900_000)]
+    trace = tmp_path / "run"
+    trace.mkdir()
+    with open(trace / "bench_kernel_trace.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for r in rows:
+            f.write(f'{r[0]},"{r[1]}",{r[2]},{r[3]}\n')
+    flops = 4 * 2 * 16 * 4096 ** 2 * 128
+    line = {"value": 1.0, "ms_per_step": 0.301, "steps": steps, "warmup": warm,
+            "config": {"workload": "w", "B": 2, "H": 16, "N": 4096, "d": 128},
+            "roofline": {"peak": 2500.0, "achieved": flops / 251e-6 / 1e12, "frac": flops / 251e-6 / 2.5e15},
+            "extra": {"settle_launches": settle, "settle_ms": 3.0, "kernel_ms_mean": 0.251,
+                      "kernel_ms_median": 0.251, "kernel_ms_min": 0.241, "interval_ms_mean": 0.301}}
+    line_file = tmp_path / "line.txt"
+    line_file.write_text("log text\n" + json.dumps(line) + "\n")
+    out = tmp_path / "summary.md"
+    profiling.summarize_bench(str(trace), str(line_file), "python3 bench.py", str(out))
+    text = out.read_text()
+    assert "| timed region: average duration / time per launch | 300.0 us |" in text
+    assert "| kernel-bound events: average duration | 250.0 us | 251.0 us |" in text
+    assert "| min duration | 240.0 us | 241.0 us |" in text
+    assert f"{flops / 250e-6 / 2.5e15:.4f}" in text
+    assert "launches 14..17" in text

@@ -353,6 +353,43 @@ def test_merge_of_gpu_key_ranges_equals_whole():
 
 
 # ---------------------------------------------------------------------------
+# attn_fwd_ex_timed: attn_fwd_ex's results, and events around its attention
+# kernel alone
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,B,H,Nq,Nk,d,causal,splits,waves", [
+    ("bf16", 1, 2, 1000, 1000, 128, False, 1, "8"),  # ping-pong kernel, ragged tail
+    ("bf16", 1, 4, 1024, 1024, 64, False, 1, None),  # keys split between the wave groups
+    ("bf16", 1, 2, 700, 700, 64, True, 3, "4"),      # mask, key splits and the merge
+    ("bf16", 2, 2, 1, 2000, 128, False, 0, None),    # one query per head, split, merged
+    ("fp32", 1, 1, 256, 256, 64, False, 1, None),    # 16-query fp32 kernel
+    ("fp32", 1, 2, 130, 300, 128, True, 2, None),    # fp32 with the mask, split, merged
+])
+def test_fwd_ex_timed(dtype, B, H, Nq, Nk, d, causal, splits, waves, monkeypatch):
+    if waves is not None:
+        monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    w = _wl(B, H, Nq, Nk, d, dtype=dtype, seed=60 + Nq % 7, causal=causal)
+    x = _cuda(make_inputs(w))
+    o1, lse1 = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal, num_splits=splits)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    outer0, outer1, start, stop = ev(), ev(), ev(), ev()
+    outer0.record()
+    o2, lse2 = ta.attn_fwd_ex_timed(x["q"], x["k"], x["v"], start, stop, w.scale, causal=causal,
+                                    num_splits=splits)
+    outer1.record()
+    o3, lse3 = ta.attn_fwd_ex_timed(x["q"], x["k"], x["v"], None, None, w.scale, causal=causal,
+                                    num_splits=splits)
+    torch.cuda.synchronize()
+    # Same kernels on the same inputs: bitwise the same results.
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    assert torch.equal(o1, o3) and torch.equal(lse1, lse3)
+    tol, rel = (FP32_TOL, None) if dtype == "fp32" else (BF16_TOL, BF16_REL)
+    _check(x, o2, lse2, w.scale, causal, tol, rel)
+    inner, outer = start.elapsed_time(stop), outer0.elapsed_time(outer1)
+    assert 0.0 < inner <= outer + 1e-3, (inner, outer)
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads of these paths, whole outputs
 # ---------------------------------------------------------------------------
 

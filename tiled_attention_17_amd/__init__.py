@@ -14,7 +14,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_timed", "attn_fwd_ex_workspace_bytes", "attn_fwd_ex_auto_splits",
            "attn_merge", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_matmul_nt",
            "attn_quantize_mxfp8", "attn_fwd_mxfp8", "attn_bwd_ex_noalloc", "ATTN_NOALLOC_MAX_ROWS",
            "library", "AttnError",
@@ -66,6 +66,8 @@ def library():
     lib.attn_fwd_ex.restype = ctypes.c_int
     lib.attn_fwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_f,
                                 ctypes.c_int, c_i64, c_vp, ctypes.c_size_t, ctypes.c_int, c_vp]
+    lib.attn_fwd_ex_timed.restype = ctypes.c_int
+    lib.attn_fwd_ex_timed.argtypes = lib.attn_fwd_ex.argtypes + [c_vp, c_vp]
     lib.attn_merge.restype = ctypes.c_int
     lib.attn_merge.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
                                ctypes.c_int, c_vp]
@@ -180,6 +182,34 @@ def attn_fwd_ex(q, k, v, scale=None, *, causal=False, num_splits=1, out=None, ls
     2..128 = that many key ranges merged afterwards, 0 = the library's choice.
     The split workspace is allocated here unless given.
     """
+    return _fwd_ex(q, k, v, scale, causal, num_splits, out, lse, workspace, stream, None)
+
+
+def attn_fwd_ex_timed(q, k, v, start, stop, scale=None, *, causal=False, num_splits=1, out=None,
+                      lse=None, workspace=None, stream=None):
+    """attn_fwd_ex that binds two timing events to its attention kernel (see attn_fwd_ex_timed).
+
+    start, stop: torch.cuda.Event(enable_timing=True) or None. After the
+    stream has reached the call, start.elapsed_time(stop) is the attention
+    kernel's own execution time in ms. torch creates an event's HIP handle on
+    its first record, so an event not yet recorded is recorded once here,
+    on the same stream, before the call.
+    """
+    return _fwd_ex(q, k, v, scale, causal, num_splits, out, lse, workspace, stream, (start, stop))
+
+
+def _event_handle(ev, device, stream):
+    import torch
+    if ev is None:
+        return None
+    if not isinstance(ev, torch.cuda.Event):
+        raise TypeError(f"expected a torch.cuda.Event or None, got {type(ev).__name__}")
+    if not ev.cuda_event:
+        ev.record(stream if stream is not None else torch.cuda.current_stream(device))
+    return ev.cuda_event
+
+
+def _fwd_ex(q, k, v, scale, causal, num_splits, out, lse, workspace, stream, events):
     import torch
     lib = library()
     _shape4("q", q)
@@ -207,9 +237,13 @@ def attn_fwd_ex(q, k, v, scale=None, *, causal=False, num_splits=1, out=None, ls
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        st = lib.attn_fwd_ex(q.data_ptr(), _ptr(k), _ptr(v), out.data_ptr(), lse.data_ptr(),
-                             B, H, Nq, Nk, d, float(scale), mask, splits, _ptr(workspace), ws_bytes,
-                             code, _stream(dev, stream))
+        fwd_args = (q.data_ptr(), _ptr(k), _ptr(v), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                    float(scale), mask, splits, _ptr(workspace), ws_bytes, code, _stream(dev, stream))
+        if events is None:
+            st = lib.attn_fwd_ex(*fwd_args)
+        else:
+            st = lib.attn_fwd_ex_timed(*fwd_args, _event_handle(events[0], dev, stream),
+                                       _event_handle(events[1], dev, stream))
     _check(st)
     return out, lse
 

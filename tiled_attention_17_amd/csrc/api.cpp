@@ -154,7 +154,7 @@ int env_decode() {
 
 extern "C" {
 
-int attn_version(void) { return 2; }
+int attn_version(void) { return 3; }
 
 const char* attn_status_string(attn_status status) {
   switch (status) {
@@ -181,7 +181,7 @@ size_t split_workspace_bytes(int64_t rows, int64_t d, int64_t splits) {
 attn_status fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                        int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int mask,
                        int64_t num_splits, void* workspace, size_t workspace_bytes,
-                       attn_dtype dtype, void* stream) {
+                       attn_dtype dtype, void* stream, void* ev_start = nullptr, void* ev_stop = nullptr) {
   int64_t q_elems = 0, q_rows = 0, k_elems = 0, k_rows = 0;
   attn_status s = check_shape(B, H, Nq, d, dtype, &q_elems, &q_rows);
   if (s != ATTN_OK) return s;
@@ -232,6 +232,8 @@ attn_status fwd_common(const void* q, const void* k, const void* v, void* o, flo
   tattn::FwdArgs a{q, k, v, o, lse, bh, Nq, Nk, d, scale, dtype == ATTN_FP32,
                    mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves(),
                    env_ksplit(), env_decode(), env_f32_bm()};
+  a.ev_start = ev_start;
+  a.ev_stop = ev_stop;
   const hipError_t he = tattn::launch_attn_fwd(a);
   if (he != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(he));
   return ok();
@@ -274,6 +276,15 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         size_t workspace_bytes, attn_dtype dtype, void* stream) {
   return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, (int)mask, num_splits, workspace,
                     workspace_bytes, dtype, stream);
+}
+
+attn_status attn_fwd_ex_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                              attn_mask mask, int64_t num_splits, void* workspace,
+                              size_t workspace_bytes, attn_dtype dtype, void* stream,
+                              void* start_event, void* stop_event) {
+  return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, (int)mask, num_splits, workspace,
+                    workspace_bytes, dtype, stream, start_event, stop_event);
 }
 
 attn_status attn_matmul_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,

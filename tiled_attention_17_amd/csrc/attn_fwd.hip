@@ -36,6 +36,8 @@
 //     zeros for them.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "launch.h"
 #include "tile_common.h"
@@ -1517,30 +1519,37 @@ static FwdParams make_params(const FwdArgs& a, int bm, int64_t* total_out) {
   return p;
 }
 
+// The one launch of an attention kernel in a forward call. The caller's
+// events, when given, are bound to the start and the end of this dispatch
+// (hipExtLaunchKernel), so that their elapsed time is the kernel's own,
+// without marker commands between back-to-back launches.
+static hipError_t launch_fwd_kernel(void (*kernel)(FwdParams), int64_t total, int threads, const FwdArgs& a,
+                                    const FwdParams& p) {
+  FwdParams arg = p;
+  void* args[] = {&arg};
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)total),
+                                          dim3(threads), args, 0, (hipStream_t)a.stream, (hipEvent_t)a.ev_start,
+                                          (hipEvent_t)a.ev_stop, 0);
+  const hipError_t last = hipGetLastError();
+  return e != hipSuccess ? e : last;
+}
+
 template <int D, int NW>
 static hipError_t launch_bf16(const FwdArgs& a, const FwdParams& p, int64_t total) {
-  if constexpr (NW == 8) {
-    hipLaunchKernelGGL((attn_fwd_bf16_pingpong_kernel<D, kPingPongBN>), dim3((unsigned)total), dim3(512), 0,
-                       (hipStream_t)a.stream, p);
-  } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0,
-                       (hipStream_t)a.stream, p);
-  }
-  return hipGetLastError();
+  if constexpr (NW == 8)
+    return launch_fwd_kernel(attn_fwd_bf16_pingpong_kernel<D, kPingPongBN>, total, 512, a, p);
+  else
+    return launch_fwd_kernel(attn_fwd_bf16_kernel<D, NW>, total, NW * 64, a, p);
 }
 
 template <int D>
 static hipError_t launch_bf16_decode(const FwdArgs& a, const FwdParams& p, int64_t total) {
-  hipLaunchKernelGGL((attn_fwd_bf16_decode_kernel<D>), dim3((unsigned)total), dim3(DecodeCfg<D>::WAVES * 64), 0,
-                     (hipStream_t)a.stream, p);
-  return hipGetLastError();
+  return launch_fwd_kernel(attn_fwd_bf16_decode_kernel<D>, total, DecodeCfg<D>::WAVES * 64, a, p);
 }
 
 template <int D, int NW>
 static hipError_t launch_bf16_ksplit(const FwdArgs& a, const FwdParams& p, int64_t total) {
-  hipLaunchKernelGGL((attn_fwd_bf16_ksplit_kernel<D, NW>), dim3((unsigned)total), dim3(2 * NW * 64), 0,
-                     (hipStream_t)a.stream, p);
-  return hipGetLastError();
+  return launch_fwd_kernel(attn_fwd_bf16_ksplit_kernel<D, NW>, total, 2 * NW * 64, a, p);
 }
 
 // Whether to split a workgroup's keys between two wave groups: for unmasked
@@ -1556,19 +1565,11 @@ static bool use_ksplit(const FwdArgs& a, int64_t splits, int nw) {
 template <int D>
 static hipError_t launch_f32(const FwdArgs& a, const FwdParams& p, int64_t total, bool ksplit, bool small) {
   if constexpr (D == 64) {
-    if (small) {
-      hipLaunchKernelGGL((attn_fwd_f32_ksplit16_kernel<D>), dim3((unsigned)total),
-                         dim3(FwdF32Split16Cfg<D>::NG * 64), 0, (hipStream_t)a.stream, p);
-      return hipGetLastError();
-    }
+    if (small)
+      return launch_fwd_kernel(attn_fwd_f32_ksplit16_kernel<D>, total, FwdF32Split16Cfg<D>::NG * 64, a, p);
   }
-  if (ksplit)
-    hipLaunchKernelGGL((attn_fwd_f32_ksplit_kernel<D>), dim3((unsigned)total),
-                       dim3(FwdF32SplitCfg<D>::NG * 64), 0, (hipStream_t)a.stream, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)total), dim3(FwdF32Cfg<D>::THREADS), 0,
-                       (hipStream_t)a.stream, p);
-  return hipGetLastError();
+  if (ksplit) return launch_fwd_kernel(attn_fwd_f32_ksplit_kernel<D>, total, FwdF32SplitCfg<D>::NG * 64, a, p);
+  return launch_fwd_kernel(attn_fwd_f32_kernel<D>, total, FwdF32Cfg<D>::THREADS, a, p);
 }
 
 // fp32: split each workgroup's keys between its waves (32 queries per

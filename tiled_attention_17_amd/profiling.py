@@ -29,8 +29,9 @@
       profiles/fwd_bf16_n4096_d128_kernel_stats.md: every kernel's calls and
       average duration, and the headline forward's timed launches picked out
       of the trace by launch order (bench.py launches the headline first:
-      settle_launches + warmup untimed launches, then `steps` timed ones),
-      with their average duration and roofline fraction beside the line's.
+      settle_launches + warmup untimed launches, then `steps` launches of the
+      timed region, then `steps` launches with kernel-bound events), with
+      their average duration and roofline fraction beside the line's.
 
   python -m tiled_attention_17_amd.profiling mfma-ceiling [--iters 1200] [--settle-ms 500] [--out-md FILE]
       Runs the matrix-core probe (libtattn_probe.so, csrc/mfma_ceiling.hip)
@@ -353,12 +354,14 @@ def summarize_bench(trace_dir, bench_line, cmd, out_md):
     disp = sorted(((int(r["Dispatch_Id"]), _short(r["Kernel_Name"]),
                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in trace))
     fwd = [ns for _, k, ns in disp if k.startswith(FWD_KERNEL)]
-    timed = fwd[untimed:untimed + steps]
+    region = fwd[untimed:untimed + steps]
+    timed = fwd[untimed + steps:untimed + 2 * steps]
     if len(timed) != steps:
-        raise SystemExit(f"trace holds {len(fwd)} forward launches, fewer than {untimed} + {steps}")
+        raise SystemExit(f"trace holds {len(fwd)} forward launches, fewer than {untimed} + 2 * {steps}")
     flops = 4 * line["config"]["B"] * line["config"]["H"] * line["config"]["N"] ** 2 * line["config"]["d"]
     peak = line["roofline"]["peak"] * 1e12
     avg_us = sum(timed) / steps / 1e3
+    region_us = sum(region) / steps / 1e3
     srt = sorted(timed)
     frac_trace = flops / (avg_us * 1e-6) / peak
     groups = {}
@@ -374,20 +377,25 @@ def summarize_bench(trace_dir, bench_line, cmd, out_md):
         f"    {cmd}", "",
         "## Headline forward: the timed launches", "",
         f"bench.py launched the headline forward {ex['settle_launches']} times to settle the clock "
-        f"({ex['settle_ms']:.0f} ms of GPU time), {warm} warm-up times, then {steps} timed times. "
-        f"The timed launches are forward launches {untimed + 1}..{untimed + steps} of the trace "
-        "(the headline is the first workload bench.py runs).", "",
-        "| figure | kernel trace (timed launches) | bench.py line (HIP events) |",
+        f"({ex['settle_ms']:.0f} ms of GPU time), {warm} warm-up times, then {steps} times back to back "
+        f"in the timed region (forward launches {untimed + 1}..{untimed + steps} of the trace: `value`, "
+        f"`ms_per_step`), then {steps} times with start and stop events bound to each kernel (launches "
+        f"{untimed + steps + 1}..{untimed + 2 * steps}: `roofline.achieved`). The headline is the first "
+        "workload bench.py runs.", "",
+        "| figure | kernel trace | bench.py line (HIP events) |",
         "|---|---|---|",
-        f"| average duration | {avg_us:.1f} us | {ex['kernel_ms_mean'] * 1e3:.1f} us |",
+        f"| timed region: average duration / time per launch | {region_us:.1f} us | "
+        f"{ex.get('interval_ms_mean', float('nan')) * 1e3:.1f} us from one kernel's end to the next "
+        f"one's; {line['ms_per_step'] * 1e3:.1f} us per step |",
+        f"| kernel-bound events: average duration | {avg_us:.1f} us | {ex['kernel_ms_mean'] * 1e3:.1f} us |",
         f"| median duration | {srt[steps // 2] / 1e3:.1f} us | {ex['kernel_ms_median'] * 1e3:.1f} us |",
         f"| min duration | {srt[0] / 1e3:.1f} us | {ex['kernel_ms_min'] * 1e3:.1f} us |",
         f"| TFLOP/s at 4·B·H·N²·d = {flops / 1e9:.1f} GFLOP | {flops / (avg_us * 1e-6) / 1e12:.1f} | "
         f"{line['roofline']['achieved']:.1f} |",
         f"| roofline frac (peak {line['roofline']['peak']:.0f} TFLOP/s) | {frac_trace:.4f} | "
         f"{line['roofline']['frac']:.4f} |", "",
-        f"Line vs trace: {100.0 * (line['roofline']['frac'] / frac_trace - 1):+.1f} % (the events also hold "
-        "the dispatch gap between back-to-back launches).", "",
+        f"Line vs trace: {100.0 * (line['roofline']['frac'] / frac_trace - 1):+.1f} % (the bound start "
+        "event marks the end of a marker command just before the kernel's dispatch).", "",
         "## Every kernel of the run (rocprofv3 kernel trace; durations in us)", "",
         "| kernel | calls | average | min | max |", "|---|---|---|---|---|"]
     for k, (n, tot, mn, mx) in sorted(groups.items(), key=lambda kv: -kv[1][1]):
