@@ -143,6 +143,10 @@ int env_f32_bm() {
   return (b == 16 || b == 32) ? b : 0;
 }
 
+// TILED_ATTN_BWD_DKDV_WAVES=4 or 8 fixes the waves per workgroup of the
+// dK/dV sweep (128 or 256 keys per workgroup).
+int env_dkdv_waves() { return env_int("TILED_ATTN_BWD_DKDV_WAVES", {4, 8}); }
+
 // TILED_ATTN_FWD_DECODE=1 keeps bf16 launches with one query per head on
 // the tiled kernels instead of the one-query kernel.
 int env_decode() {
@@ -471,6 +475,7 @@ attn_status bwd_common(const void* q, const void* k, const void* v, const void* 
   if ((s = device_cus(&cus)) != ATTN_OK) return s;
   tattn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B * H, Nq, Nk, d, scale,
                    mask == ATTN_MASK_CAUSAL, stream, cus};
+  a.dkdv_waves = env_dkdv_waves();
   const hipError_t e = noalloc ? tattn::launch_attn_bwd_noalloc(a) : tattn::launch_attn_bwd(a);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -48,12 +48,17 @@ namespace tattn {
 // ---------------------------------------------------------------------------
 // 2. dK, dV
 // ---------------------------------------------------------------------------
-// One workgroup per 256 keys: 8 waves of 32 keys, two per SIMD. Each wave
-// keeps K^T of its keys in VGPRs (a B operand); the V rows of the
-// workgroup's keys sit in LDS for the whole sweep. The query tiles stream
-// through LDS in stages of 64 (Q and dO rows by buffer_load ... lds,
-// double-buffered), each processed as two sub-steps of 32 queries with the
-// key in the lane:
+// One workgroup per 32 NW keys: NW waves of 32 keys. With NW = 8 one
+// workgroup fills a compute unit (two waves per SIMD); with NW = 4 two
+// workgroups share one (one wave of each per SIMD), which halves the
+// workgroup size for grids that would leave compute units idle or run a
+// partial last round. Each wave keeps K^T of its keys in VGPRs (a B
+// operand); the V rows of the workgroup's keys sit in LDS for the whole
+// sweep. The query tiles stream through LDS in stages of BQ queries (Q and
+// dO rows by buffer_load ... lds, double-buffered; BQ = 64, or 32 for
+// NW = 4 at d = 128, where two workgroups' stages of 64 would not fit in
+// LDS), each processed as sub-steps of 32 queries with the key in the
+// lane:
 //   S = Q K^T and dP = dO V^T         (Q, dO rows as A operands; K^T from
 //                                      VGPRs, V rows from LDS as B operands)
 //   P = 2^(c S - LSE2), dS = P (dP - D)  (LSE2 and D per accumulator slot)
@@ -66,24 +71,24 @@ namespace tattn {
 // ceil(x / m) for m > 0, and 0 for x <= 0.
 __device__ __forceinline__ int ceil_div_nonneg(int x, int m) { return x > 0 ? (x + m - 1) / m : 0; }
 
-template <int D>
+template <int D, int NW_>
 struct DkdvTile {
-  static constexpr int NW = 8;
+  static constexpr int NW = NW_;
   static constexpr int BKV = 32 * NW;   // keys per workgroup
-  static constexpr int BQ = 64;         // queries per stage
+  static constexpr int BQ = NW == 8 || D == 64 ? 64 : 32;  // queries per stage
   static constexpr int QTILE = BQ * D;  // one Q or dO stage, bf16 elements
   static constexpr int DK = D / 16;
   static constexpr int DB = D / 32;
 };
 
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                           const bf16* __restrict__ V, const bf16* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dv,
                           bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int BH,
                           int n_ktiles, int total_tiles, float c, float scale, int causal, int remap) {
-  using C = DkdvTile<D>;
+  using C = DkdvTile<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16 smem[C::BKV * D + 4 * C::QTILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][C::BQ];  // [buf][lse2 | D][query]
   bf16* const vs = smem;
@@ -256,7 +261,7 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     if (more) stage(j + 1, cur ^ 1);
     if (MODE != 0) {
 #pragma unroll 1
-      for (int u = 0; u < 2; ++u) substep(std::integral_constant<bool, MODE == 1>{}, cur, j, u);
+      for (int u = 0; u < C::BQ / 32; ++u) substep(std::integral_constant<bool, MODE == 1>{}, cur, j, u);
     }
     if (more) store_stats(cur ^ 1);
     wait_vmem();
@@ -266,14 +271,14 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // branch inside a loop body, which would make the accumulators' live
   // ranges fork): stages before j_vis hold no visible pair, stages from
   // j_all on hold only visible pairs, and the mask edge of 32 keys crosses
-  // at most two 64-query stages in between. Every wave runs every stage's
-  // barrier.
+  // at most two stages (of 32 or 64 queries) in between. Every wave runs
+  // every stage's barrier.
   int j_vis = j0, j_all = j0;
   if (kw_lo >= Nk) {
     j_vis = j_all = max(j0, n_st);
   } else if (causal) {
-    // first stage with a visible pair: 64 j + 63 + off >= kw_lo;
-    // first stage with all pairs visible: 64 j + off >= kw_lo + 31
+    // first stage with a visible pair: BQ j + BQ - 1 + off >= kw_lo;
+    // first stage with all pairs visible: BQ j + off >= kw_lo + 31
     j_vis = min(max(j0, ceil_div_nonneg(kw_lo - off - (C::BQ - 1), C::BQ)), max(j0, n_st));
     j_all = min(max(j_vis, ceil_div_nonneg(kw_lo + 31 - off, C::BQ)), max(j0, n_st));
   }
@@ -769,6 +774,34 @@ constexpr auto dq_kernel() {
 }
 
 // ---------------------------------------------------------------------------
+template <int D, int NW>
+static hipError_t launch_dkdv(const BwdArgs& a, float c) {
+  constexpr int BKV = DkdvTile<D, NW>::BKV;
+  const int n_kt = (int)((a.Nk + BKV - 1) / BKV);
+  const int64_t total = a.BH * n_kt;
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NW>), dim3((unsigned)total), dim3(NW * 64), 0,
+                     (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                     (const bf16*)a.dout, a.lse, a.row_dot, (bf16*)a.dk, (bf16*)a.dv, (int)a.Nq, (int)a.Nk,
+                     (int)a.BH, n_kt, (int)total, c, a.scale, a.causal ? 1 : 0,
+                     (int)(!a.causal && total % 8 == 0));
+  return hipGetLastError();
+}
+
+// Waves per dK/dV workgroup. At d = 64 the 4-wave workgroups (two per
+// compute unit) measured as fast or faster on every shape tried. At
+// d = 128 they hold stages of 32 queries (twice the barriers and stage
+// transfers), which costs ≈1.5 % on grids of whole rounds of 8-wave
+// workgroups, but their finer grain wins where the 8-wave grid would
+// leave compute units idle or end in a partial round (wave quantization,
+// CS336 Lecture 5 notes §6.2).
+int dkdv_waves(const BwdArgs& a) {
+  if (a.dkdv_waves == 4 || a.dkdv_waves == 8) return a.dkdv_waves;
+  if (a.d == 64) return 4;
+  const int64_t g8 = a.BH * ((a.Nk + 255) / 256);
+  return (g8 % a.num_cus == 0 || g8 >= 4 * (int64_t)a.num_cus) ? 8 : 4;
+}
+
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   const hipStream_t st = (hipStream_t)a.stream;
@@ -795,16 +828,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (a.Nk > 0) {
-    constexpr int BKV = DkdvTile<D>::BKV;
-    const int n_kt = (int)((a.Nk + BKV - 1) / BKV);
-    const int64_t total = a.BH * n_kt;
-    if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)total), dim3(512), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
-                       a.lse, a.row_dot, (bf16*)a.dk, (bf16*)a.dv, (int)a.Nq, (int)a.Nk, (int)a.BH,
-                       n_kt, (int)total, c, a.scale, a.causal ? 1 : 0,
-                       (int)(!a.causal && total % 8 == 0));
-    hipError_t e = hipGetLastError();
+    const hipError_t e = dkdv_waves(a) == 8 ? launch_dkdv<D, 8>(a, c) : launch_dkdv<D, 4>(a, c);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -86,7 +86,11 @@ struct BwdArgs {
   bool causal;      // query i sees key j iff j <= i + Nk - Nq
   void* stream;
   int num_cus;
+  int dkdv_waves = 0;  // 0 = choose; 4 or 8 = waves per dK/dV workgroup (128 or 256 keys)
 };
+
+// Waves per workgroup of the dK/dV sweep for these arguments (4 or 8).
+int dkdv_waves(const BwdArgs& a);
 
 hipError_t launch_attn_fwd(const FwdArgs& a);
 
