@@ -451,11 +451,13 @@ def _check_bwd(x, o, dq, dk, dv, scale, causal, heads=None):
 @pytest.mark.parametrize("Nq,Nk", [(1, 1), (64, 64), (200, 200), (513, 513), (100, 700), (700, 100),
                                    (300, 129), (1, 1000), (777, 1100), (1100, 777), (1536, 1536)])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("dkdv_waves", ["4", "8"])
-def test_bwd_ex_small(Nq, Nk, d, causal, dkdv_waves, monkeypatch):
-    # Both dK/dV workgroup shapes (128 keys in 4 waves, 256 keys in 8) on
-    # every case, whichever the library would pick for the shape.
-    monkeypatch.setenv("TILED_ATTN_BWD_DKDV_WAVES", dkdv_waves)
+@pytest.mark.parametrize("waves", ["4", "8"])
+def test_bwd_ex_small(Nq, Nk, d, causal, waves, monkeypatch):
+    # Both workgroup shapes of each sweep (dK/dV: 128 keys in 4 waves or 256
+    # in 8; dQ: 128 queries in 4 waves, lock-step, or 256 in 8) on every case,
+    # whichever the library would pick for the shape.
+    monkeypatch.setenv("TILED_ATTN_BWD_DKDV_WAVES", waves)
+    monkeypatch.setenv("TILED_ATTN_BWD_DQ_WAVES", waves)
     w = _wl(1, 2, Nq, Nk, d, seed=60 + Nq + Nk + d)
     x = _cuda(make_inputs(w, with_grad_output=True))
     o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, causal=causal)

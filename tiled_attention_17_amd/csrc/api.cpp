@@ -147,6 +147,10 @@ int env_f32_bm() {
 // dK/dV sweep (128 or 256 keys per workgroup).
 int env_dkdv_waves() { return env_int("TILED_ATTN_BWD_DKDV_WAVES", {4, 8}); }
 
+// TILED_ATTN_BWD_DQ_WAVES=4 or 8 fixes the waves per workgroup of the dQ
+// sweep (4: 128 queries, lock-step; 8: 256 queries).
+int env_dq_waves() { return env_int("TILED_ATTN_BWD_DQ_WAVES", {4, 8}); }
+
 // TILED_ATTN_FWD_DECODE=1 keeps bf16 launches with one query per head on
 // the tiled kernels instead of the one-query kernel.
 int env_decode() {
@@ -476,6 +480,7 @@ attn_status bwd_common(const void* q, const void* k, const void* v, const void* 
   tattn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B * H, Nq, Nk, d, scale,
                    mask == ATTN_MASK_CAUSAL, stream, cus};
   a.dkdv_waves = env_dkdv_waves();
+  a.dq_waves = env_dq_waves();
   const hipError_t e = noalloc ? tattn::launch_attn_bwd_noalloc(a) : tattn::launch_attn_bwd(a);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -343,9 +343,9 @@ __device__ __forceinline__ float row_term(const bf16* orow, const bf16x8* dof, b
   return d;
 }
 
-template <int D>
+template <int D, int NW_ = 8>
 struct DqTile {
-  static constexpr int NW = 8;
+  static constexpr int NW = NW_;
   static constexpr int BM = 32 * NW;
   using T = FwdTile<D, 64>;
   static constexpr int STAGE = 3 * T::KTILE;  // K rows, V rows, K^T
@@ -436,15 +436,15 @@ __device__ __forceinline__ void dq_scores_to_ds(const f32x16* sacc, const f32x16
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                         const bf16* __restrict__ V, const bf16* __restrict__ O,
                         const bf16* __restrict__ dO, const float* __restrict__ LSE,
                         float* __restrict__ Dv,
                         bf16* __restrict__ dQ, int Nq, int Nk, int BH, int n_qtiles, int total_tiles,
                         float c, float scale, int causal, int remap) {
-  using C = DqTile<D>;
+  using C = DqTile<D, NW>;
   using T = typename C::T;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
   auto ks = [&](int b) { return smem + b * C::STAGE; };
@@ -492,7 +492,7 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const VtOffsets vo(lq, h);
   const KOffsets<D, true> ko(lq, h);
   const KDirect<D, 64, C::NW> kd(0, wave, lane);
-  KtStager<D> st(tid);  // K^T through registers
+  KtStager<D, NW> st(tid);  // K^T through registers
   auto stage_direct = [&](int j, int buf) {
     kd.template load<true>(Kh, Nk, j, 64, ks(buf));
     kd.template load<true>(Vh, Nk, j, 64, vs(buf));
@@ -766,11 +766,36 @@ void attn_bwd_dq_pingpong_kernel(const bf16* __restrict__ Q, const bf16* __restr
   }
 }
 
-// The dQ sweep launched for head dimension D (see launch_bwd_d).
-template <int D>
-constexpr auto dq_kernel() {
-  if constexpr (D == 128) return &attn_bwd_dq_pingpong_kernel<D>;
-  else return &attn_bwd_dq_kernel<D>;
+// One launch of the dQ sweep: the lock-step kernel with NW waves per
+// workgroup (32 NW queries), or the 8-wave ping-pong kernel.
+template <int D, int NW, bool PINGPONG>
+static hipError_t launch_dq(const BwdArgs& a, float c) {
+  constexpr int BM = DqTile<D, NW>::BM;
+  const int n_qt = (int)((a.Nq + BM - 1) / BM);
+  const int64_t total = a.BH * n_qt;
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  auto kernel = PINGPONG ? &attn_bwd_dq_pingpong_kernel<D> : &attn_bwd_dq_kernel<D, NW>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(NW * 64), 0, (hipStream_t)a.stream,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,
+                     (const bf16*)a.dout, a.lse, a.row_dot, (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH,
+                     n_qt, (int)total, c, a.scale, a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
+  return hipGetLastError();
+}
+
+// Waves per dQ workgroup (4: 128 queries, lock-step; 8: 256 queries, the
+// ping-pong sweep at d = 128 and the lock-step one at d = 64). At d = 128
+// a tile's MFMA phase (48 products) is longer than its dS phase and the
+// ping-pong sweep overlaps the two (its 96 KiB of LDS leave room for one
+// workgroup per compute unit, so it keeps 8 waves); at d = 64 (24 products)
+// the dS work dominates and the lock-step sweep, with half the barriers,
+// is faster, and its 4-wave workgroups (two per compute unit) win where
+// the 8-wave grid would leave compute units idle or end in a partial
+// round, as in the dK/dV sweep.
+int dq_waves(const BwdArgs& a) {
+  if (a.dq_waves == 4 || a.dq_waves == 8) return a.dq_waves;
+  if (a.d != 64) return 8;
+  const int64_t g8 = a.BH * ((a.Nq + 255) / 256);
+  return (g8 % a.num_cus == 0 || g8 >= 4 * (int64_t)a.num_cus) ? 8 : 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -804,7 +829,6 @@ int dkdv_waves(const BwdArgs& a) {
 
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
-  const hipStream_t st = (hipStream_t)a.stream;
   const float c = a.scale * kLog2e;
   // The dQ sweep runs first: it also writes the row terms D_i that the
   // dK/dV sweep reads. With no query, the dK/dV kernel alone runs (it writes
@@ -812,19 +836,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
   // (likewise).
   const int64_t rows = a.BH * a.Nq;
   if (rows > 0) {
-    constexpr int BM = DqTile<D>::BM;
-    const int n_qt = (int)((a.Nq + BM - 1) / BM);
-    const int64_t total = a.BH * n_qt;
-    if (total > INT32_MAX) return hipErrorInvalidValue;
-    // At d = 128 a tile's MFMA phase (48 products) is longer than its dS
-    // phase and the ping-pong sweep overlaps the two; at d = 64 (24
-    // products) the dS work dominates and the lock-step sweep, with half the
-    // barriers, is faster.
-    hipLaunchKernelGGL(dq_kernel<D>(), dim3((unsigned)total), dim3(512), 0, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o, (const bf16*)a.dout, a.lse,
-                       a.row_dot, (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH, n_qt, (int)total, c,
-                       a.scale, a.causal ? 1 : 0, (int)(!a.causal && total % 8 == 0));
-    hipError_t e = hipGetLastError();
+    const hipError_t e = dq_waves(a) == 4 ? launch_dq<D, 4, false>(a, c) : launch_dq<D, 8, D == 128>(a, c);
     if (e != hipSuccess) return e;
   }
   if (a.Nk > 0) {

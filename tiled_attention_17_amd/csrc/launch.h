@@ -87,10 +87,12 @@ struct BwdArgs {
   void* stream;
   int num_cus;
   int dkdv_waves = 0;  // 0 = choose; 4 or 8 = waves per dK/dV workgroup (128 or 256 keys)
+  int dq_waves = 0;    // 0 = choose; 4 or 8 = waves per dQ workgroup (128 or 256 queries)
 };
 
-// Waves per workgroup of the dK/dV sweep for these arguments (4 or 8).
+// Waves per workgroup of the dK/dV and dQ sweeps for these arguments (4 or 8).
 int dkdv_waves(const BwdArgs& a);
+int dq_waves(const BwdArgs& a);
 
 hipError_t launch_attn_fwd(const FwdArgs& a);
 
