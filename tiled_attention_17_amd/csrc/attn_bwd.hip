@@ -437,7 +437,7 @@ __device__ __forceinline__ void dq_scores_to_ds(const f32x16* sacc, const f32x16
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 && NW == 4 ? 1 : 2, 2)))
 void attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                         const bf16* __restrict__ V, const bf16* __restrict__ O,
                         const bf16* __restrict__ dO, const float* __restrict__ LSE,

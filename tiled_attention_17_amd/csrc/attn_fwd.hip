@@ -773,9 +773,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_decode_kernel(const FwdPara
         __builtin_amdgcn_make_buffer_rsrc((void*)(Vh + (size_t)key0 * D), 0, rows * D * 2, kBufferRsrcWord3);
     u32x4 kk[C::U], vv[C::U];
 #pragma unroll
-    for (int i = 0; i < C::U; ++i) kk[i] = buffer_load16(krs, ((i * C::KPI + kg) * D + 8 * ch) * 2);
+    for (int i = 0; i < C::U; ++i) kk[i] = buffer_load16_stream(krs, ((i * C::KPI + kg) * D + 8 * ch) * 2);
 #pragma unroll
-    for (int i = 0; i < C::U; ++i) vv[i] = buffer_load16(vrs, ((i * C::KPI + kg) * D + 8 * ch) * 2);
+    for (int i = 0; i < C::U; ++i) vv[i] = buffer_load16_stream(vrs, ((i * C::KPI + kg) * D + 8 * ch) * 2);
 
     // Scores in the exp2 domain (c = scale log2 e); keys the query does not
     // see (past the split's range or the causal window) get -inf.
