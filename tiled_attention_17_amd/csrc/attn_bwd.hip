@@ -9,7 +9,9 @@
 //   dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
 // Two launches on the caller's stream, no atomics (deterministic):
-//   1. dq:       one workgroup per 256 queries; each wave keeps Q^T and dO^T
+//   1. dq:       one workgroup per 256 queries (or, at d = 64 on grids that
+//                would not fill whole rounds of the chip, per 128 queries,
+//                two workgroups per compute unit); each wave keeps Q^T and dO^T
 //                of its 32 queries in VGPRs, first forms the row terms
 //                D_i = sum_k dO_ik O_ik of its queries (and writes them for
 //                the second launch), then sweeps the key tiles, computing
@@ -17,10 +19,12 @@
 //                then dQ^T += K^T dS^T; at d = 128 in the forward's ping-pong
 //                schedule (one wave's dS work under the other's products on
 //                each SIMD);
-//   2. dkdv:     one workgroup per 256 keys; each wave keeps K^T of its 32
+//   2. dkdv:     one workgroup per 256 keys (or per 128 keys, two per
+//                compute unit, at d = 64 and on grids that would not fill
+//                whole rounds); each wave keeps K^T of its 32
 //                keys in VGPRs, the workgroup keeps the V rows of its keys
-//                in LDS, and the query tiles stream through LDS (64 queries
-//                per stage, two sub-steps of 32), computing S = Q K^T and
+//                in LDS, and the query tiles stream through LDS (64 or 32
+//                queries per stage, sub-steps of 32), computing S = Q K^T and
 //                dP = dO V^T with the key in the lane so that P and dS feed
 //                dV^T += dO^T P and dK^T += Q^T dS as B operands; dO^T and
 //                Q^T come from ds_read_b64_tr_b16 transposed reads of the
@@ -310,7 +314,8 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 // ---------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------
-// One workgroup per 256 queries: 8 waves of 32 queries, two per SIMD. Each
+// One workgroup per 32 NW queries: NW waves of 32 queries, two per SIMD
+// (NW = 8: one workgroup per compute unit; NW = 4: two). Each
 // wave keeps Q^T and dO^T of its queries in VGPRs (B operands) and sweeps the
 // key tiles of 64 keys, with the query in the lane throughout:
 //   S^T = K Q^T and dP^T = V dO^T   (K, V row-major in LDS, as the forward's
