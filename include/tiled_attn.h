@@ -104,7 +104,8 @@ const char* attn_last_error(void);
  * for splitting a workgroup's keys between its waves (bf16: two wave groups
  * of an unmasked launch; fp32: the four waves of a 32-query workgroup);
  * TILED_ATTN_FWD_DECODE = 1 keeps bf16 launches with one query per head on
- * the tiled kernels instead of the one-query kernel.
+ * the tiled kernels instead of the one-query kernel; TILED_ATTN_FWD_F32_BM =
+ * 16 or 32 fixes the query tile of the fp32 key-split kernel at d = 64.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,
@@ -273,6 +274,11 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn
  *   dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i, dS = P * (dP - D),
  *   dQ = scale dS K, dK = scale dS^T Q.
  * bf16 only (ATTN_FP32 returns ATTN_ERR_UNSUPPORTED).
+ * The library picks the workgroup shapes of its two sweeps from the grid
+ * size; TILED_ATTN_BWD_DKDV_WAVES = 4 or 8 (128 or 256 keys per dK/dV
+ * workgroup) and TILED_ATTN_BWD_DQ_WAVES = 4 or 8 (128 or 256 queries per
+ * dQ workgroup) override that choice, for tests and experiments; the
+ * results are bit-identical either way.
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
