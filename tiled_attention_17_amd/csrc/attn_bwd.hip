@@ -779,7 +779,10 @@ static hipError_t launch_dq(const BwdArgs& a, float c) {
   const int n_qt = (int)((a.Nq + BM - 1) / BM);
   const int64_t total = a.BH * n_qt;
   if (total > INT32_MAX) return hipErrorInvalidValue;
-  auto kernel = PINGPONG ? &attn_bwd_dq_pingpong_kernel<D> : &attn_bwd_dq_kernel<D, NW>;
+  constexpr auto kernel = [] {
+    if constexpr (PINGPONG) return &attn_bwd_dq_pingpong_kernel<D>;
+    else return &attn_bwd_dq_kernel<D, NW>;
+  }();
   hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(NW * 64), 0, (hipStream_t)a.stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,
                      (const bf16*)a.dout, a.lse, a.row_dot, (bf16*)a.dq, (int)a.Nq, (int)a.Nk, (int)a.BH,
