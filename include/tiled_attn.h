@@ -105,7 +105,9 @@ const char* attn_last_error(void);
  * of an unmasked launch; fp32: the four waves of a 32-query workgroup);
  * TILED_ATTN_FWD_DECODE = 1 keeps bf16 launches with one query per head on
  * the tiled kernels instead of the one-query kernel; TILED_ATTN_FWD_F32_BM =
- * 16 or 32 fixes the query tile of the fp32 key-split kernel at d = 64.
+ * 16 or 32 fixes the query tile of the fp32 key-split kernel at d = 64,
+ * and TILED_ATTN_FWD_KSPLIT_BN = 64 or 128 the key tile of the bf16
+ * key-split kernel at d = 64.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,

@@ -184,6 +184,23 @@ def test_causal_ignores_hidden_keys():
 # N_q != N_k, with and without the mask (N_q > N_k leaves rows with no key)
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("bn", ["64", "128"])
+@pytest.mark.parametrize("waves", ["2", "4"])
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 2, 100, 1000), (2, 1, 257, 1024), (1, 1, 64, 1500), (1, 2, 300, 129),
+                                       (1, 1, 2, 2048), (1, 3, 513, 4100)])
+def test_keys_split_tile_sizes_d64(B, H, Nq, Nk, waves, bn, monkeypatch):
+    # The bf16 key split at d = 64 with 64- and 128-key tiles (the launch
+    # picks 128 for large grids of long key ranges), ragged key ends included.
+    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT", "2")
+    monkeypatch.setenv("TILED_ATTN_FWD_WAVES", waves)
+    monkeypatch.setenv("TILED_ATTN_FWD_KSPLIT_BN", bn)
+    w = _wl(B, H, Nq, Nk, 64, seed=70 + Nq + Nk)
+    x = _cuda(make_inputs(w))
+    o, lse = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale)
+    torch.cuda.synchronize()
+    _check(x, o, lse, w.scale, False, BF16_TOL, BF16_REL)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("waves,ksplit", [("2", "1"), ("4", "1"), ("8", "1"), ("2", "2"), ("4", "2")])
 @pytest.mark.parametrize("Nq,Nk", [(1, 1000), (100, 700), (300, 129), (513, 64), (64, 2048)])

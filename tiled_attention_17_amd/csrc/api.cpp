@@ -151,6 +151,10 @@ int env_dkdv_waves() { return env_int("TILED_ATTN_BWD_DKDV_WAVES", {4, 8}); }
 // sweep (4: 128 queries, lock-step; 8: 256 queries).
 int env_dq_waves() { return env_int("TILED_ATTN_BWD_DQ_WAVES", {4, 8}); }
 
+// TILED_ATTN_FWD_KSPLIT_BN=64 or 128 fixes the key tile of the bf16
+// key-split kernel at d = 64.
+int env_ksplit_bn() { return env_int("TILED_ATTN_FWD_KSPLIT_BN", {64, 128}); }
+
 // TILED_ATTN_FWD_DECODE=1 keeps bf16 launches with one query per head on
 // the tiled kernels instead of the one-query kernel.
 int env_decode() {
@@ -240,6 +244,7 @@ attn_status fwd_common(const void* q, const void* k, const void* v, void* o, flo
   tattn::FwdArgs a{q, k, v, o, lse, bh, Nq, Nk, d, scale, dtype == ATTN_FP32,
                    mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves(),
                    env_ksplit(), env_decode(), env_f32_bm()};
+  a.ksplit_bn = env_ksplit_bn();
   a.ev_start = ev_start;
   a.ev_stop = ev_stop;
   const hipError_t he = tattn::launch_attn_fwd(a);

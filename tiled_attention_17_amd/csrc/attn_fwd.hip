@@ -437,12 +437,15 @@ void attn_fwd_bf16_kernel(const FwdParams p) {
 // without a second launch. Unmasked launches only: the ragged end of the
 // key range is the only masked tile, and it is group 1's last.
 // ---------------------------------------------------------------------------
-// At D = 128 the four tile stages take 128 KiB of LDS, so one workgroup fits
+// Key tiles of BN = 64 keys, or 128 at d = 64 (half the barriers per key,
+// each step's products twice as many; the four tile stages then take
+// 128 KiB of LDS, as at D = 128 with 64-key tiles), so one workgroup fits
 // on a compute unit: with NW = 2 that is one wave per SIMD.
-template <int D, int NW>
+template <int D, int NW, int BN>
 __global__ __launch_bounds__(2 * NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 && NW == 2 ? 1 : 2, 2)))
 void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
-  using T = FwdTile<D>;
+  static_assert(BN == 64 || (BN == 128 && D == 64), "128-key tiles only at d = 64");
+  using T = FwdTile<D, BN>;
   constexpr int BM = 32 * NW;
   constexpr int NE = 16 * T::DB + 2;  // floats one lane hands over: o, m, l
   static_assert(NW * NE * 64 * 4 <= 4 * T::STAGE * 2, "hand-over must fit the tile buffers");
@@ -488,10 +491,10 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
   // The next tile's K goes straight to LDS and its whole V into registers
   // at the start of a step; V is transposed into LDS after the step's value
   // product, so its loads have the whole step to arrive.
-  const KDirect<D, 64, NW> kd(0, wave, lane);
-  Stager<D, 64, NW * 64, 64, false> st;
+  const KDirect<D, BN, NW> kd(0, wave, lane);
+  Stager<D, BN, NW * 64, BN, false> st;
   if (my_n > 0) {
-    kd.load(Kh, p.Nk, t0, 64, ks(0));
+    kd.load(Kh, p.Nk, t0, BN, ks(0));
     st.load(krs, vrs, t0, t0, 0, gtid);
     st.store(ks(0), vs(0), 0, gtid);
   }
@@ -504,15 +507,18 @@ void attn_fwd_bf16_ksplit_kernel(const FwdParams p) {
     const int cur = i & 1;
     const bool more = i + 1 < my_n;
     if (more) {
-      kd.template load<true>(Kh, p.Nk, t0 + i + 1, 64, ks(cur ^ 1));
+      kd.template load<true>(Kh, p.Nk, t0 + i + 1, BN, ks(cur ^ 1));
       st.load(krs, vrs, t0 + i + 1, t0 + i + 1, 0, gtid);
     }
-    f32x16 sacc[2];
-    u32x4 pw[4];
-    score_tile<D>(ks(cur), qf, ko, sacc);
-    softmax_tile<MASKED, T::DB>(sacc, p.c, kr.k_begin + (my_first + i) * T::BN, kmax, h, m_run, l_run,
-                                oacc, pw);
-    pv_tile<D>(vs(cur), pw, vo, oacc);
+    f32x16 sacc[T::NKB];
+    u32x4 pw[T::NT];
+    // A 128-key tile is two 64-key halves: K rows 64.. and the second V^T sub-tile.
+#pragma unroll
+    for (int hf = 0; hf < BN / 64; ++hf) score_tile<D>(ks(cur) + hf * 64 * D, qf, ko, sacc + 2 * hf);
+    softmax_tile<MASKED, T::DB, T::NKB>(sacc, p.c, kr.k_begin + (my_first + i) * T::BN, kmax, h, m_run,
+                                        l_run, oacc, pw);
+#pragma unroll
+    for (int hf = 0; hf < BN / 64; ++hf) pv_tile<D>(vs(cur) + hf * 64 * D, pw + 4 * hf, vo, oacc);
     if (more) st.store(ks(cur ^ 1), vs(cur ^ 1), 0, gtid);
     publish_lds();  // K tile written to LDS by its transfer, V^T by the stores
   };
@@ -1547,9 +1553,20 @@ static hipError_t launch_bf16_decode(const FwdArgs& a, const FwdParams& p, int64
   return launch_fwd_kernel(attn_fwd_bf16_decode_kernel<D>, total, DecodeCfg<D>::WAVES * 64, a, p);
 }
 
-template <int D, int NW>
+template <int D, int NW, int BN = 64>
 static hipError_t launch_bf16_ksplit(const FwdArgs& a, const FwdParams& p, int64_t total) {
-  return launch_fwd_kernel(attn_fwd_bf16_ksplit_kernel<D, NW>, total, 2 * NW * 64, a, p);
+  return launch_fwd_kernel(attn_fwd_bf16_ksplit_kernel<D, NW, BN>, total, 2 * NW * 64, a, p);
+}
+
+// Key tile of the key-split kernel at d = 64: 128 keys when the grid holds
+// more than half as many workgroups as compute units and each wave group
+// gets at least four such tiles (N_k >= 1024); fewer or shorter sweeps
+// measured faster with 64-key tiles (the 128-key pipeline's first tile and
+// hand-over weigh more there).
+static int ksplit_bn(const FwdArgs& a, int64_t total) {
+  if (a.d != 64) return 64;
+  if (a.ksplit_bn == 64 || a.ksplit_bn == 128) return a.ksplit_bn;
+  return (2 * total > (int64_t)a.num_cus && a.Nk >= 1024) ? 128 : 64;
 }
 
 // Whether to split a workgroup's keys between two wave groups: for unmasked
@@ -1665,7 +1682,9 @@ hipError_t launch_attn_fwd(const FwdArgs& a) {
   if (total > INT32_MAX) return hipErrorInvalidValue;
   hipError_t e;
   if (use_ksplit(a, splits, nw)) {
-    if (a.d == 64)
+    if (a.d == 64 && ksplit_bn(a, total) == 128)
+      e = nw == 4 ? launch_bf16_ksplit<64, 4, 128>(a, p, total) : launch_bf16_ksplit<64, 2, 128>(a, p, total);
+    else if (a.d == 64)
       e = nw == 4 ? launch_bf16_ksplit<64, 4>(a, p, total) : launch_bf16_ksplit<64, 2>(a, p, total);
     else
       e = nw == 4 ? launch_bf16_ksplit<128, 4>(a, p, total) : launch_bf16_ksplit<128, 2>(a, p, total);

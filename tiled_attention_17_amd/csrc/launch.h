@@ -29,6 +29,7 @@ struct FwdArgs {
                     // waves < 8; fp32: always)
   int decode;       // 0 = choose; 1 = never use the one-query kernel for N_q = 1 (bf16)
   int f32_bm;       // 0 = choose; 16 or 32 = query tile of the fp32 key-split kernel (d = 64)
+  int ksplit_bn = 0;  // 0 = choose; 64 or 128 = key tile of the bf16 key-split kernel (d = 64)
   void* ev_start = nullptr;  // hipEvent_t bound to the start of the attention kernel (or null)
   void* ev_stop = nullptr;   // hipEvent_t bound to its end (or null)
 };
