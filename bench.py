@@ -221,8 +221,13 @@ def measure_backward(ta, pm, dev, stream, n, settle_ms, checks):
     t = time_launches(bwd, stream, n, 3, settle_ms)
     ms = t["kernel_ms_mean"]
     fl = pm.attn_bwd_flops(w.B, w.H, w.N, w.d)
-    r = {"workload": w.name, **t, **_rates(pm, fl, pm.attn_bwd_bytes(w.B, w.H, w.N, w.d, 2), ms, "bf16"),
+    nb = pm.attn_bwd_bytes(w.B, w.H, w.N, w.d, 2)
+    r = {"workload": w.name, **t, **_rates(pm, fl, nb, ms, "bf16"),
          "flops_counted": "10·B·H·N²·d"}
+    # The same calls back to back without events between them (each call is
+    # two launches; per-call events add their own commands to every call).
+    bb = time_burst(bwd, stream, n)
+    r["back_to_back"] = {**bb, **_rates(pm, fl, nb, bb["ms_per_launch"], "bf16")}
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     checks.append({"name": w.name, "kind": "bwd", "x": x_cpu, "scale": w.scale, "heads": heads,
                    "o": o.cpu(), "lse": lse.cpu(), "grads": [t.cpu() for t in g]})
