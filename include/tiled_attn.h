@@ -174,7 +174,9 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
  *             touched.
  * A call that launches nothing (B*H*Nq == 0) or fails its checks leaves both
  * events as they were. Arguments, results and errors otherwise as for
- * attn_fwd_ex; an invalid event handle makes the launch fail (ATTN_ERR_HIP).
+ * attn_fwd_ex; a non-NULL event must be a live hipEvent_t of the current
+ * device (the library cannot check a handle: anything else is undefined),
+ * and a launch error the runtime reports returns ATTN_ERR_HIP.
  */
 attn_status attn_fwd_ex_timed(const void* q, const void* k, const void* v, void* o, float* lse,
                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
