@@ -10,6 +10,7 @@ raises immediately.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -128,8 +129,22 @@ def _shape4(name, t, shape=None, dtype=None, device=None):
 def _stream(device, stream):
     import torch
     if stream is None:
+        # torch's raw current-stream query skips building a Stream object
+        # (a few microseconds, which matter for launches of a few microseconds).
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            index = device.index if device.index is not None else torch.cuda.current_device()
+            return ctypes.c_void_p(raw(index))
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_device(device):
+    """torch.cuda.device(device), or nothing to do when it is already current."""
+    import torch
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
 
 
 def attn_fwd(q, k, v, scale=None, *, out=None, lse=None, stream=None):
@@ -154,7 +169,7 @@ def attn_fwd(q, k, v, scale=None, *, out=None, lse=None, stream=None):
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     _lse_out(lse, (B, H, N), dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H, N, d, float(scale), _dtype_code(q), _stream(dev, stream))
     _check(st)
@@ -231,7 +246,7 @@ def _fwd_ex(q, k, v, scale, causal, num_splits, out, lse, workspace, stream, eve
     _lse_out(lse, (B, H, Nq), dev)
     code = _dtype_code(q)
     mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         splits = num_splits if num_splits != 0 else attn_fwd_ex_auto_splits(B, H, Nq, Nk, d, code)
         need = attn_fwd_ex_workspace_bytes(B, H, Nq, Nk, d, splits, code)
         if workspace is None and need > 0:
@@ -272,7 +287,7 @@ def attn_merge(o_parts, lse_parts, *, dtype=None, out=None, lse=None, stream=Non
         out = torch.empty((B, H, N, d), dtype=dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), P, B, H, N, d, out.data_ptr(),
                             lse.data_ptr(), _dtype_code(out), _stream(dev, stream))
     _check(st)
@@ -305,7 +320,7 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, *, dq=None, dk=None, dv=None, work
     need = attn_bwd_workspace_bytes(B, H, N, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -342,7 +357,7 @@ def attn_bwd_ex(q, k, v, o, do, lse, scale=None, *, causal=False, dq=None, dk=No
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d,
@@ -376,7 +391,7 @@ def attn_bwd_ex_noalloc(q, k, v, o, do, lse, scale=None, *, causal=False, dq, dk
         scale = 1.0 / math.sqrt(d)
     mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
     import torch
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.attn_bwd_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                      _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, float(scale), mask,
                                      _dtype_code(q), _stream(dev, stream))
@@ -402,7 +417,7 @@ def attn_matmul_nt(a, b, *, out=None, stream=None):
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     if tuple(out.shape) != (M, N) or out.dtype != a.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous [M, N] tensor of the operands' dtype")
-    with torch.cuda.device(a.device):
+    with _on_device(a.device):
         st = lib.attn_matmul_nt(_ptr(a), _ptr(b), _ptr(out), M, N, K, _dtype_code(a),
                                 _stream(a.device, stream))
     _check(st)
@@ -432,7 +447,7 @@ def attn_quantize_mxfp8(x, *, transpose=False, stream=None):
     else:
         q = torch.empty(lead + (rows, cols), dtype=torch.uint8, device=x.device)
         sc = torch.empty(lead + (rows, max(cols // 32, 0)), dtype=torch.uint8, device=x.device)
-    with torch.cuda.device(x.device):
+    with _on_device(x.device):
         st = lib.attn_quantize_mxfp8(_ptr(x), batch, rows, cols, 1 if transpose else 0, _ptr(q), _ptr(sc),
                                      _dtype_code(x), _stream(x.device, stream))
     _check(st)
@@ -473,7 +488,7 @@ def attn_fwd_mxfp8(q8, q_scales, k8, k_scales, vt8, vt_scales, scale=None, *, ou
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    with torch.cuda.device(q8.device):
+    with _on_device(q8.device):
         st = lib.attn_fwd_mxfp8(_ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales), _ptr(vt8), _ptr(vt_scales),
                                 _ptr(out), _ptr(lse), B, H, N, d, float(scale), _stream(q8.device, stream))
     _check(st)
