@@ -228,6 +228,23 @@ def measure_backward(ta, pm, dev, stream, n, settle_ms, checks):
     # two launches; per-call events add their own commands to every call).
     bb = time_burst(bwd, stream, n)
     r["back_to_back"] = {**bb, **_rates(pm, fl, nb, bb["ms_per_launch"], "bf16")}
+    # The forward of the same inputs, for the forward + backward total at
+    # 14·B·H·N²·d (the forward's kernel time with kernel-bound events).
+    fo, flse = torch.empty_like(o), torch.empty_like(lse)
+
+    def fwd():
+        ta.attn_fwd(x["q"], x["k"], x["v"], w.scale, out=fo, lse=flse)
+
+    def fwd_timed(start, stop):
+        ta.attn_fwd_ex_timed(x["q"], x["k"], x["v"], start, stop, w.scale, out=fo, lse=flse)
+
+    tf = time_launches(fwd, stream, n, 3, 0.0, fwd_timed)
+    fwd_ms = tf["kernel_ms_mean"]
+    r["fwd_kernel_ms_mean"] = fwd_ms
+    r["fwd_bwd_ms"] = fwd_ms + ms
+    r["fwd_bwd_tflops"] = (pm.attn_fwd_flops(w.B, w.H, w.N, w.d) + fl) / ((fwd_ms + ms) * 1e-3) / 1e12
+    r["fwd_bwd_flops_counted"] = "14·B·H·N²·d"
+    del fo, flse
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     checks.append({"name": w.name, "kind": "bwd", "x": x_cpu, "scale": w.scale, "heads": heads,
                    "o": o.cpu(), "lse": lse.cpu(), "grads": [t.cpu() for t in g]})
