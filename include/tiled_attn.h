@@ -114,8 +114,10 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      attn_dtype dtype, void* stream);
 
 /* Bytes of device workspace attn_fwd_ex needs for `num_splits` key splits:
- * 0 for num_splits <= 1, else num_splits * B*H*N_q * (d + 1) * 4 (the fp32
- * partial O and LSE of every split). 0 also for invalid sizes. */
+ * 0 for num_splits = 1, else num_splits * B*H*N_q * (d + 1) * 4 (the fp32
+ * partial O and LSE of every split); for num_splits = 0, what the library's
+ * own choice needs on the current device (0 if that cannot be queried). 0
+ * also for invalid sizes. */
 size_t attn_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                                    int64_t num_splits, attn_dtype dtype);
 
@@ -140,8 +142,13 @@ int64_t attn_fwd_ex_auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, in
  *             of whole 128-key tiles (fewer when N_k is short), each range's
  *             attention is computed by its own workgroups into `workspace`
  *             as an fp32 (O_r, LSE_r) pair, and a second kernel merges them
- *             (attn_merge's rule); 0: the library's choice
- *             (attn_fwd_ex_auto_splits).
+ *             (attn_merge's rule); 0: the library's choice: the
+ *             split count attn_fwd_ex_auto_splits reports, or, for bf16
+ *             without a mask when the grid of 256-query tiles would end in
+ *             a last round of workgroups at most half full, the heads of
+ *             the whole rounds unsplit and the remaining heads split over
+ *             the keys (wave quantization, CS336 Lecture 5 notes §6.2).
+ *             Results agree with the one-pass ones within rounding.
  *   workspace device scratch of at least attn_fwd_ex_workspace_bytes() for
  *             the split count used, 16-byte aligned, owned by the caller,
  *             contents on entry ignored; must not overlap anything else.
@@ -170,8 +177,10 @@ attn_status attn_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
  *             start and the end of the call's attention kernel (its launch
  *             over the query tiles; the merge of key splits, when there is
  *             one, runs after stop_event), so that hipEventElapsedTime of the
- *             two gives that kernel's execution time. A NULL event is not
- *             touched.
+ *             two gives that kernel's execution time (with the library's
+ *             split of a partial last round, num_splits = 0, from the start
+ *             of the first of its two attention launches to the end of the
+ *             second). A NULL event is not touched.
  * A call that launches nothing (B*H*Nq == 0) or fails its checks leaves both
  * events as they were. Arguments, results and errors otherwise as for
  * attn_fwd_ex; a non-NULL event must be a live hipEvent_t of the current

@@ -406,6 +406,28 @@ def test_fwd_ex_timed(dtype, B, H, Nq, Nk, d, causal, splits, waves, monkeypatch
     assert 0.0 < inner <= outer + 1e-3, (inner, outer)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_auto_plan_splits_the_last_round(d):
+    # 288 heads of 256 queries: one whole round of 256-query workgroups on a
+    # 256-CU device and 32 heads over. With num_splits = 0 the library runs
+    # the first 256 heads unsplit and splits the keys of the other 32 (two
+    # attention launches and a merge).
+    w = _wl(1, 288, 256, 1024, d, seed=80 + d)
+    x = _cuda(make_inputs(w))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert ta.attn_fwd_ex_workspace_bytes(1, 288, 256, 1024, d, 0) == 2 * 32 * 256 * (d + 1) * 4
+    o0, l0 = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=0)
+    o1, l1 = ta.attn_fwd_ex(x["q"], x["k"], x["v"], w.scale, num_splits=1)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o2, l2 = ta.attn_fwd_ex_timed(x["q"], x["k"], x["v"], start, stop, w.scale, num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o2) and torch.equal(l0, l2)
+    assert start.elapsed_time(stop) > 0.0
+    # The heads of the whole round run the one-pass kernel on the same tiles.
+    assert torch.equal(o0[:, :256], o1[:, :256]) and torch.equal(l0[:, :256], l1[:, :256])
+    _check_whole(x, o0, l0, w.scale, False)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads of these paths, whole outputs
 # ---------------------------------------------------------------------------

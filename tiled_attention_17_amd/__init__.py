@@ -247,7 +247,9 @@ def _fwd_ex(q, k, v, scale, causal, num_splits, out, lse, workspace, stream, eve
     code = _dtype_code(q)
     mask = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
     with _on_device(dev):
-        splits = num_splits if num_splits != 0 else attn_fwd_ex_auto_splits(B, H, Nq, Nk, d, code)
+        # num_splits = 0 goes through as 0: the library's own choice, whose
+        # workspace attn_fwd_ex_workspace_bytes(..., 0) reports.
+        splits = num_splits
         need = attn_fwd_ex_workspace_bytes(B, H, Nq, Nk, d, splits, code)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)

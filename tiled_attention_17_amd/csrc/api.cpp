@@ -216,7 +216,11 @@ attn_status fwd_common(const void* q, const void* k, const void* v, void* o, flo
   const int64_t bh = B * H;
   int64_t splits = num_splits == 0 ? tattn::fwd_auto_splits(bh, Nq, Nk, dtype == ATTN_FP32, cus) : num_splits;
   if (k_rows == 0) splits = 1;
-  const size_t need = split_workspace_bytes(q_rows, d, splits);
+  tattn::FwdTailPlan tail{0, 0};
+  const bool use_tail = num_splits == 0 && splits == 1 && k_rows > 0 &&
+                        tattn::fwd_tail_plan(bh, Nq, Nk, dtype == ATTN_FP32, mask == ATTN_MASK_CAUSAL, cus, &tail);
+  const size_t need = use_tail ? split_workspace_bytes((bh - tail.head_split) * Nq, d, tail.tail_splits)
+                               : split_workspace_bytes(q_rows, d, splits);
   if (need > 0) {
     if ((s = check_ptr(workspace, "workspace", 16)) != ATTN_OK) return s;
     if (workspace_bytes < need)
@@ -245,6 +249,10 @@ attn_status fwd_common(const void* q, const void* k, const void* v, void* o, flo
                    mask == ATTN_MASK_CAUSAL, (int)splits, (float*)workspace, stream, cus, env_waves(),
                    env_ksplit(), env_decode(), env_f32_bm()};
   a.ksplit_bn = env_ksplit_bn();
+  if (use_tail) {
+    a.tail_heads = bh - tail.head_split;
+    a.tail_splits = tail.tail_splits;
+  }
   a.ev_start = ev_start;
   a.ev_stop = ev_stop;
   const hipError_t he = tattn::launch_attn_fwd(a);
@@ -269,6 +277,18 @@ size_t attn_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
   if (check_shape(B, H, Nq, d, dtype, &elems, &rows) != ATTN_OK) return 0;
   if (check_shape(B, H, Nk, d, dtype, &ke, &kr) != ATTN_OK) return 0;
   if (num_splits < 0 || num_splits > tattn::kMaxSplits) return 0;
+  if (num_splits == 0 && rows > 0 && kr > 0) {
+    // The library's own choice on the current device.
+    int cus = 0;
+    if (device_cus(&cus) != ATTN_OK) return 0;
+    const bool fp32 = dtype == ATTN_FP32;
+    const int64_t bh = B * H;
+    tattn::FwdTailPlan tail{0, 0};
+    const int64_t splits = tattn::fwd_auto_splits(bh, Nq, Nk, fp32, cus);
+    if (splits == 1 && tattn::fwd_tail_plan(bh, Nq, Nk, fp32, false, cus, &tail))
+      return split_workspace_bytes((bh - tail.head_split) * Nq, d, tail.tail_splits);
+    return split_workspace_bytes(rows, d, splits);
+  }
   return split_workspace_bytes(rows, d, num_splits);
 }
 

@@ -1654,7 +1654,61 @@ int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) 
   return clamp_splits((2 * (int64_t)num_cus + tiles - 1) / tiles, 2);
 }
 
+// Wave quantization of the last round (CS336 Lecture 5 notes §6.2): a bf16
+// grid of 256-query tiles whose workgroup count exceeds the CU count by a
+// remainder of at most half the CUs runs that remainder as a round of its own
+// with most of the chip idle. Splitting the keys of only the heads in that
+// last round fills the chip for it; measured with the two launches made
+// separately: 18 heads of N = 4096 (a last round 1/8 full) 200.7 -> 155.8 µs,
+// 20 heads (1/4) 201.1 -> 167.5 µs, 24 heads (1/2) 208.7 -> 195.0 µs, 40
+// heads (2.5 rounds) 319.4 -> 311.8 µs.
+bool fwd_tail_plan(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, bool causal, int num_cus, FwdTailPlan* plan) {
+  if (fp32 || causal || Nq < 128 || num_cus <= 0 || BH < 2) return false;
+  if (fwd_bf16_waves(BH, Nq, 1, num_cus) != 8) return false;
+  const int64_t tpw = (Nq + 255) / 256;  // 256-query tiles per head
+  const int64_t total = BH * tpw;
+  const int64_t rem = total % num_cus;
+  if (total <= num_cus || rem == 0 || 2 * rem > num_cus) return false;
+  const int64_t head_split = (total - rem) / tpw;  // heads of the whole rounds
+  const int64_t tail = BH - head_split;
+  if (head_split < 1 || tail < 1 || head_split * tpw < num_cus) return false;
+  const int s = fwd_auto_splits(tail, Nq, Nk, false, num_cus);
+  if (s < 2) return false;
+  plan->head_split = head_split;
+  plan->tail_splits = s;
+  return true;
+}
+
+static hipError_t launch_attn_fwd_one(const FwdArgs& a);
+
 hipError_t launch_attn_fwd(const FwdArgs& a) {
+  if (a.tail_heads <= 0) return launch_attn_fwd_one(a);
+  // The heads of the whole rounds, unsplit, then the tail heads with their
+  // key splits, on the same stream. The caller's start event goes with the
+  // first attention launch, the stop event with the second.
+  const int64_t h1 = a.BH - a.tail_heads;
+  FwdArgs b = a;
+  b.BH = h1;
+  b.n_splits = 1;
+  b.tail_heads = 0;
+  b.ev_stop = nullptr;
+  hipError_t e = launch_attn_fwd_one(b);
+  if (e != hipSuccess) return e;
+  FwdArgs t = a;
+  const size_t qo = (size_t)h1 * a.Nq * a.d * 2, kv = (size_t)h1 * a.Nk * a.d * 2;
+  t.q = (const char*)a.q + qo;
+  t.k = (const char*)a.k + kv;
+  t.v = (const char*)a.v + kv;
+  t.o = (char*)a.o + qo;
+  t.lse = a.lse + (size_t)h1 * a.Nq;
+  t.BH = a.tail_heads;
+  t.n_splits = a.tail_splits;
+  t.tail_heads = 0;
+  t.ev_start = nullptr;
+  return launch_attn_fwd_one(t);
+}
+
+static hipError_t launch_attn_fwd_one(const FwdArgs& a) {
   int64_t total = 0;
   if (a.dtype_fp32) {
     const bool ks = use_f32_ksplit(a), small = use_f32_small(a, ks);

@@ -30,6 +30,8 @@ struct FwdArgs {
   int decode;       // 0 = choose; 1 = never use the one-query kernel for N_q = 1 (bf16)
   int f32_bm;       // 0 = choose; 16 or 32 = query tile of the fp32 key-split kernel (d = 64)
   int ksplit_bn = 0;  // 0 = choose; 64 or 128 = key tile of the bf16 key-split kernel (d = 64)
+  int64_t tail_heads = 0;  // > 0: heads [BH - tail_heads, BH) run with tail_splits splits (fwd_tail_plan)
+  int tail_splits = 0;
   void* ev_start = nullptr;  // hipEvent_t bound to the start of the attention kernel (or null)
   void* ev_stop = nullptr;   // hipEvent_t bound to its end (or null)
 };
@@ -65,6 +67,16 @@ constexpr int kMaxSplits = 128;  // largest number of key splits of one forward 
 int64_t split_keys_for(int64_t Nk, int n_splits);
 // Number of key splits the library picks when the caller leaves it open.
 int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus);
+
+// The library's plan for a grid whose last round of workgroups would be at
+// most half full: the heads [0, head_split) run unsplit in whole rounds, the
+// remaining heads with tail_splits key splits (and a merge) over the whole
+// chip. Returns false (no such plan) where it does not apply.
+struct FwdTailPlan {
+  int64_t head_split;
+  int tail_splits;
+};
+bool fwd_tail_plan(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, bool causal, int num_cus, FwdTailPlan* plan);
 hipError_t launch_attn_merge(const float* o_part, const float* lse_part, int n_parts, int64_t rows,
                              int64_t d, void* o, float* lse, bool out_fp32, void* stream);
 
