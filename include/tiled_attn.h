@@ -122,9 +122,13 @@ size_t attn_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                                    int64_t num_splits, attn_dtype dtype);
 
 /* Number of key splits attn_fwd_ex picks with num_splits = 0 on the current
- * device: 1 when the query tiles alone give every compute unit work, else
- * enough splits for about two workgroups per compute unit (each split at
- * least 256 keys), at most 128. 0 on invalid sizes or a HIP error. */
+ * device: 1 when the query tiles alone give every compute unit work; else,
+ * for bf16 with at least 128 queries, enough splits of the 256-query tiles
+ * to fill the chip once if each split keeps at least 2048 keys, otherwise
+ * splits of the smaller tiles for about two workgroups per compute unit
+ * (each at least 256 keys); with one query per head about one workgroup per
+ * compute unit (each split at least 512 keys); at most 128. 0 on invalid
+ * sizes or a HIP error. */
 int64_t attn_fwd_ex_auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                                 attn_dtype dtype);
 

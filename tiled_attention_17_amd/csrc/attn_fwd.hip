@@ -1628,7 +1628,9 @@ int fwd_bf16_waves(int64_t BH, int64_t Nq, int64_t splits, int num_cus) {
 // tiles are split until they fill the chip once (each split keeping at least
 // four 128-key tiles); with fewer, the smaller tiles are split for about two
 // workgroups per compute unit (each split at least two 128-key tiles).
-int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) {
+// min_pp_tiles: the fewest 128-key tiles a split of the 256-query ping-pong
+// tiles may hold.
+static int auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus, int64_t min_pp_tiles) {
   const int64_t key_tiles = (Nk + kSplitAlign - 1) / kSplitAlign;
   auto clamp_splits = [&](int64_t s, int64_t min_tiles) -> int {
     s = s < key_tiles / min_tiles ? s : key_tiles / min_tiles;
@@ -1645,13 +1647,29 @@ int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) 
   if (!fp32 && Nq >= 128) {
     const int64_t t8 = BH * ((Nq + 255) / 256);
     if (t8 >= num_cus) return 1;
-    const int s = clamp_splits((num_cus + t8 - 1) / t8, 4);
-    if (s > 1) return s;
+    const int s = clamp_splits((num_cus + t8 - 1) / t8, min_pp_tiles);
+    // Split the 256-query tiles only where that fills at least half a round.
+    if (s > 1 && 2 * t8 * s >= num_cus) return s;
   }
   const int bm = fp32 ? FwdF32Cfg<64>::BM : 32 * fwd_bf16_waves(BH, Nq, 1, num_cus);
   const int64_t tiles = BH * ((Nq + bm - 1) / bm);
   if (tiles <= 0 || tiles >= num_cus) return 1;
-  return clamp_splits((2 * (int64_t)num_cus + tiles - 1) / tiles, 2);
+  return clamp_splits((2 * (int64_t)num_cus + tiles - 1) / tiles, fp32 ? 2 : 4);
+}
+
+// Split counts of a whole launch: splits of the ping-pong tiles keep at
+// least 16 key tiles (2048 keys) and fill at least half a round. With
+// shorter ranges the smaller unsplit tiles measured faster than a split and
+// its merge (B=1 H=16 N=2048: 41.6 µs unsplit in 4-wave tiles against 48.9
+// µs with 2 splits; B=2 H=10 N=2048 66.2 against 74.6), with 2048 keys a
+// split measured equal or better (B=1 H=12 N=4096: 121.2 against 127.4 µs),
+// and the query shard's long range (16384 keys) gains most (308 -> 244 µs).
+// Grids too small for that split the smaller tiles instead, each split at
+// least 4 key tiles in bf16 (B=1 H=2 N=4096: 4 splits 36.7 µs against 59.1
+// µs for 2 splits of the ping-pong tiles; B=1 H=4 N=2048: 27.6 against 33.1
+// µs unsplit).
+int fwd_auto_splits(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, int num_cus) {
+  return auto_splits(BH, Nq, Nk, fp32, num_cus, 16);
 }
 
 // Wave quantization of the last round (CS336 Lecture 5 notes §6.2): a bf16
@@ -1672,7 +1690,9 @@ bool fwd_tail_plan(int64_t BH, int64_t Nq, int64_t Nk, bool fp32, bool causal, i
   const int64_t head_split = (total - rem) / tpw;  // heads of the whole rounds
   const int64_t tail = BH - head_split;
   if (head_split < 1 || tail < 1 || head_split * tpw < num_cus) return false;
-  const int s = fwd_auto_splits(tail, Nq, Nk, false, num_cus);
+  // The tail heads alone leave most of the chip idle: their splits may be
+  // as short as 4 key tiles (2 heads of N = 4096: 8 splits).
+  const int s = auto_splits(tail, Nq, Nk, false, num_cus, 4);
   if (s < 2) return false;
   plan->head_split = head_split;
   plan->tail_splits = s;
